@@ -1,0 +1,197 @@
+/*
+ * attn_decode.h -- C ABI of the split-KV decode / small-query attention
+ * library for MI355X (gfx950).
+ *
+ * What the library computes (for each batch b, query position i, query head
+ * hq, with KV head h = hq / G, G = Hq / Hkv, and the L valid keys of b):
+ *
+ *     O[b,i,hq,:] = sum_j softmax_j(scale * q . k_j) v_j
+ *     LSE[b,hq,i] = ln sum_j exp(scale * q . k_j)
+ *
+ * This is the attention definition of the "SmallQ FlashAttention (Vector)"
+ * README (section 接口) with the grouped-query sharing of the lpnh.cn
+ * "pack_gqa 与 num_splits" article; the default scale is 1/sqrt(head_dim).
+ * It is evaluated with online softmax (ai6s.net FlashAttention article,
+ * section "FlashAttention 的数学细节"), over num_splits KV ranges whose
+ * partial outputs and logsumexps are merged at the end (lpnh.cn article,
+ * section "两个开关在 kernel 层面各做了什么").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers to tensors are DEVICE pointers owned by the caller.  The
+ *   library never allocates, frees or keeps them; it keeps no state between
+ *   calls except the thread-local record read by attn_last_plan().
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Work is enqueued on it and the call returns without waiting.
+ * - All arguments are validated on the host before anything is enqueued.
+ *   On any error nothing is launched and no output byte is written.
+ * - Device-side data (block_table entries, cache_seqlens values) is the
+ *   caller's contract: every block_table entry a sequence uses must name a
+ *   page < num_pages, and 0 <= cache_seqlens[b] <= max_seqlen_k.  Use
+ *   attn_check_paged_inputs() on host copies to verify it in tests.
+ * - Element types: q, k, v and out share one 16-bit type (ATTN_FP16 or
+ *   ATTN_BF16); lse is float32.  Accumulation is float32 throughout.
+ * - An empty sequence (L = 0) gives O = 0 and LSE = -inf.
+ * - Tensors must be contiguous in the layouts stated below, 16-byte
+ *   aligned for q/k/v/out and 4-byte aligned for lse, block_table and
+ *   cache_seqlens; workspace must be 256-byte aligned.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    ATTN_ERR_SHAPE = 2,       /* sizes are inconsistent (<= 0, Hq % Hkv != 0,   */
+                              /* max_seqlen_k > max_pages_per_seq * page_size)  */
+    ATTN_ERR_UNSUPPORTED = 3, /* valid, but outside the supported envelope      */
+    ATTN_ERR_ARG = 4,         /* num_splits / pack_gqa / scale out of range     */
+    ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than plan requires   */
+    ATTN_ERR_ALIGN = 6,       /* a pointer breaks the alignment rule            */
+    ATTN_ERR_HIP = 7,         /* the HIP runtime reported an error              */
+    ATTN_ERR_DATA = 8         /* attn_check_paged_inputs found a bad entry      */
+} attn_status;
+
+typedef enum { ATTN_FP16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Paged decode problem.
+ *   q, out        [batch, q_len, num_heads_q, head_dim]
+ *   k_cache,
+ *   v_cache       [num_pages, page_size, num_heads_kv, head_dim]
+ *                 (block, token-in-block, head, dim: the PA_BBND layout of
+ *                 the MixedQuantSparseFlashMlaMetadata article, section
+ *                 参数说明)
+ *   block_table   int32 [batch, max_pages_per_seq]; key j of sequence b is
+ *                 slot j % page_size of page block_table[b][j / page_size]
+ *   cache_seqlens int32 [batch], number of valid keys of each sequence
+ *   lse           float32 [batch, num_heads_q, q_len]
+ * Supported: head_dim in {64, 128}; page_size a multiple of 16; q_len >= 1
+ * (no causal mask: every query row sees all L keys); any G = Hq / Hkv. */
+typedef struct {
+    int32_t batch;
+    int32_t q_len;
+    int32_t num_heads_q;
+    int32_t num_heads_kv;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t max_pages_per_seq;
+    int32_t max_seqlen_k;  /* upper bound of cache_seqlens; drives the plan   */
+    int32_t dtype;         /* attn_dtype                                       */
+} attn_decode_shape;
+
+/* Dense small-query problem (the SmallQ README's [heads, qLen, headDim]
+ * layout, with num_heads_kv <= num_heads_q sharing as above).
+ *   q, out  [num_heads_q, q_len, head_dim]
+ *   k, v    [num_heads_kv, kv_len, head_dim]
+ *   lse     float32 [num_heads_q, q_len]
+ * Supported: head_dim in {64, 128}; any kv_len >= 0; q_len >= 1. */
+typedef struct {
+    int32_t num_heads_q;
+    int32_t num_heads_kv;
+    int32_t q_len;
+    int32_t kv_len;
+    int32_t head_dim;
+    int32_t dtype;
+} attn_dense_shape;
+
+/* What a call runs.  Filled by the plan functions and recorded by every
+ * forward call (see attn_last_plan). */
+typedef struct {
+    int32_t num_splits;      /* S: KV ranges per (sequence, head unit)        */
+    int32_t pack_gqa;        /* 1: the G query heads of a KV head share a unit */
+    int32_t rows_per_unit;   /* query rows per unit: q_len*G packed, q_len not */
+    int32_t rows_per_block;  /* rows one workgroup carries (1, 2, 4 or 8)      */
+    int32_t row_blocks;      /* ceil(rows_per_unit / rows_per_block)           */
+    int32_t units;           /* batch * head units * row_blocks               */
+    int32_t grid;            /* workgroups of the split kernel = units * S    */
+    int32_t split_granule;   /* split ranges are multiples of this many keys   */
+    int32_t num_cus;         /* compute units the plan was made for           */
+    int32_t combine;         /* 1 when a combine pass merges S > 1 partials   */
+    int32_t kernel;          /* kernel variant id (diagnostic)                */
+    int32_t reserved;
+    int64_t workspace_bytes; /* bytes of workspace the forward call needs     */
+} attn_plan;
+
+/* Plan a paged decode call without touching any device.
+ *   num_splits: 0 = choose by rule, >= 1 = use this value (<= 1024).
+ *   pack_gqa:  -1 = choose by rule, 0 = off, 1 = on (forced on when S > 1).
+ *   num_cus:    compute units to plan for; 0 = 256 (one MI355X).
+ * The rules are the lpnh.cn article's (section "pack_gqa 怎么选": row
+ * efficiency with a 0.9 margin; section "num_splits 怎么选": one split when
+ * the units reach 80% of the compute units or the KV spans at most 4 tiles
+ * of 128 keys, else the smallest split count whose last-wave efficiency is
+ * within 85% of the best), taken over compute units with an M tile of 16. */
+attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int pack_gqa,
+                             int num_cus, attn_plan* plan);
+
+/* Paged decode forward (layouts above).
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *   lse may be NULL (not written).
+ *   workspace / workspace_bytes: device scratch of at least
+ *     plan.workspace_bytes (0 when S = 1, then workspace may be NULL).
+ *     Contents on return: float32 partial outputs [S][rows][head_dim]
+ *     followed (at the next 256-byte boundary) by float32 partial LSEs
+ *     [S][rows], rows ordered (b, i, hq).
+ * The plan uses the compute-unit count of the current device. */
+attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* cache_seqlens, int num_splits, int pack_gqa,
+                            float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Plan a dense call (num_splits as above; always packed). */
+attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,
+                            attn_plan* plan);
+
+/* Dense small-query forward (layouts above; other arguments as in
+ * attn_decode_fwd; partial rows ordered (hq, i)). */
+attn_status attn_dense_fwd(const attn_dense_shape* shape, const void* q, const void* k,
+                           const void* v, int num_splits, float softmax_scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Merge S partials into the final output (the combine step on its own).
+ *   o_part   float32 [num_splits][rows][head_dim], rows = batch*q_len*num_heads
+ *            ordered (b, i, h); lse_part float32 [num_splits][rows]
+ *            (natural log; -inf marks an empty partial).
+ *   out      16-bit [batch, q_len, num_heads, head_dim]
+ *   lse      float32 [batch, num_heads, q_len], may be NULL.
+ * Per row: M = max_s LSE_s, w_s = exp(LSE_s - M), O = sum w_s O_s / sum w_s,
+ * LSE = M + ln sum w_s; all partials empty gives O = 0, LSE = -inf.
+ * head_dim: any value in [1, 512]. */
+attn_status attn_combine_fwd(int num_splits, int batch, int q_len, int num_heads, int head_dim,
+                             int dtype, const float* o_part, const float* lse_part, void* out,
+                             float* lse, void* stream);
+
+/* Host check of the device-data contract on host copies of block_table
+ * [batch, max_pages_per_seq] and cache_seqlens [batch]: every used entry in
+ * [0, num_pages) and 0 <= L <= max_seqlen_k.  Returns ATTN_ERR_DATA and the
+ * first offending sequence in *bad_batch (may be NULL) on failure. */
+attn_status attn_check_paged_inputs(const attn_decode_shape* shape,
+                                    const int32_t* block_table_host,
+                                    const int32_t* cache_seqlens_host, int64_t num_pages,
+                                    int32_t* bad_batch);
+
+/* Plan recorded by the last successful forward call on this thread
+ * (ATTN_ERR_ARG if none yet). */
+attn_status attn_last_plan(attn_plan* plan);
+
+/* Static text for a status code. */
+const char* attn_status_str(attn_status status);
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

@@ -110,7 +110,8 @@ def _p(a):
 
 
 def default_threads():
-    return os.cpu_count() or 1
+    """Worker threads: every host core, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 def decode16(bits, dtype):

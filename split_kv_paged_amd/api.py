@@ -1,0 +1,198 @@
+"""torch-facing binding of the C ABI.
+
+PyTorch provides device memory and the stream; every step of the attention
+runs in the library's HIP kernels.  Functions here check tensor placement,
+dtype and layout, allocate outputs / workspace with torch when the caller
+does not pass them, and call the library on torch's current stream.
+"""
+import ctypes
+import math
+
+import torch
+
+from . import lib as _L
+
+_DT = {torch.float16: _L.FP16, torch.bfloat16: _L.BF16}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def decode_shape(q, k_cache, block_table, max_seqlen_k=None):
+    B, qlen, hq, d = q.shape
+    _, page, hkv, d2 = k_cache.shape
+    _need(d2 == d, "q and k_cache head_dim differ")
+    maxp = block_table.shape[1]
+    if max_seqlen_k is None:
+        max_seqlen_k = maxp * page
+    return _L.DecodeShape(B, qlen, hq, hkv, d, page, maxp, int(max_seqlen_k), _DT[q.dtype])
+
+
+def decode_plan(batch, q_len, num_heads_q, num_heads_kv, head_dim, page_size, max_pages_per_seq,
+                max_seqlen_k, dtype=torch.bfloat16, num_splits=0, pack_gqa=-1, num_cus=0):
+    """Host-only plan (no device touched)."""
+    shape = _L.DecodeShape(batch, q_len, num_heads_q, num_heads_kv, head_dim, page_size,
+                           max_pages_per_seq, max_seqlen_k,
+                           _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype))
+    plan = _L.Plan()
+    _L.check("attn_decode_plan",
+             _L.load().attn_decode_plan(ctypes.byref(shape), num_splits, pack_gqa, num_cus,
+                                        ctypes.byref(plan)))
+    return plan
+
+
+def dense_plan(num_heads_q, num_heads_kv, q_len, kv_len, head_dim, dtype=torch.float16,
+               num_splits=0, num_cus=0):
+    shape = _L.DenseShape(num_heads_q, num_heads_kv, q_len, kv_len, head_dim,
+                          _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype))
+    plan = _L.Plan()
+    _L.check("attn_dense_plan",
+             _L.load().attn_dense_plan(ctypes.byref(shape), num_splits, num_cus,
+                                       ctypes.byref(plan)))
+    return plan
+
+
+def last_plan():
+    plan = _L.Plan()
+    _L.check("attn_last_plan", _L.load().attn_last_plan(ctypes.byref(plan)))
+    return plan
+
+
+def _check_dev(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t is None:
+            continue
+        _need(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    return dev
+
+
+def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pack_gqa=-1,
+               softmax_scale=None, max_seqlen_k=None, out=None, lse=None, return_lse=True,
+               workspace=None, stream=None):
+    """Paged decode attention.
+
+    q [B, q_len, Hq, d] fp16/bf16; k_cache, v_cache [pages, page, Hkv, d];
+    block_table int32 [B, max_pages]; cache_seqlens int32 [B].
+    Returns (out [B, q_len, Hq, d], lse float32 [B, Hq, q_len] or None).
+    max_seqlen_k (a host int bound on cache_seqlens) drives the plan; by
+    default it is max_pages * page_size, which needs no device sync.
+    """
+    _need(q.dtype in _DT and k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
+          "q, k_cache, v_cache must share fp16 or bf16")
+    _need(block_table.dtype == torch.int32 and cache_seqlens.dtype == torch.int32,
+          "block_table and cache_seqlens must be int32")
+    dev = _check_dev(q, k_cache, v_cache, block_table, cache_seqlens, out, lse, workspace)
+    shape = decode_shape(q, k_cache, block_table, max_seqlen_k)
+    lib = _L.load()
+    plan = _L.Plan()
+    with torch.cuda.device(dev):
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        _L.check("attn_decode_plan", lib.attn_decode_plan(ctypes.byref(shape), num_splits,
+                                                          pack_gqa, cus, ctypes.byref(plan)))
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and return_lse:
+            lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
+                              device=dev)
+        if workspace is None and plan.workspace_bytes > 0:
+            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        code = lib.attn_decode_fwd(
+            ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(cache_seqlens), num_splits, pack_gqa,
+            float(softmax_scale) if softmax_scale else 0.0, _ptr(out), _ptr(lse),
+            _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _L.check("attn_decode_fwd", code)
+    return out, lse
+
+
+def dense_fwd(q, k, v, num_splits=0, softmax_scale=None, out=None, lse=None, return_lse=True,
+              workspace=None, stream=None):
+    """Dense small-query attention: q [Hq, q_len, d], k/v [Hkv, kv_len, d].
+
+    Returns (out [Hq, q_len, d], lse float32 [Hq, q_len] or None).
+    """
+    _need(q.dtype in _DT and k.dtype == q.dtype and v.dtype == q.dtype,
+          "q, k, v must share fp16 or bf16")
+    dev = _check_dev(q, k, v, out, lse, workspace)
+    hq, qlen, d = q.shape
+    hkv, kvlen, d2 = k.shape
+    _need(d2 == d and tuple(v.shape) == tuple(k.shape), "k/v shapes")
+    shape = _L.DenseShape(hq, hkv, qlen, kvlen, d, _DT[q.dtype])
+    lib = _L.load()
+    plan = _L.Plan()
+    with torch.cuda.device(dev):
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        _L.check("attn_dense_plan", lib.attn_dense_plan(ctypes.byref(shape), num_splits, cus,
+                                                        ctypes.byref(plan)))
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and return_lse:
+            lse = torch.empty((hq, qlen), dtype=torch.float32, device=dev)
+        if workspace is None and plan.workspace_bytes > 0:
+            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        code = lib.attn_dense_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), num_splits,
+                                  float(softmax_scale) if softmax_scale else 0.0, _ptr(out),
+                                  _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _L.check("attn_dense_fwd", code)
+    return out, lse
+
+
+def combine_fwd(o_part, lse_part, batch, q_len, num_heads, dtype=torch.bfloat16, out=None,
+                lse=None, stream=None):
+    """Merge partials: o_part float32 [S, rows, d], lse_part float32 [S, rows],
+    rows ordered (b, i, h).  Returns (out [batch, q_len, heads, d], lse [batch, heads, q_len])."""
+    _need(o_part.dtype == torch.float32 and lse_part.dtype == torch.float32, "float32 partials")
+    S, rows, d = o_part.shape
+    _need(rows == batch * q_len * num_heads and tuple(lse_part.shape) == (S, rows), "shapes")
+    dev = _check_dev(o_part, lse_part, out, lse)
+    if out is None:
+        out = torch.empty((batch, q_len, num_heads, d), dtype=dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, num_heads, q_len), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        code = _L.load().attn_combine_fwd(S, batch, q_len, num_heads, d, _DT[out.dtype],
+                                          _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
+                                          _stream(dev, stream))
+    _L.check("attn_combine_fwd", code)
+    return out, lse
+
+
+def workspace_partials(workspace, plan, nrows, head_dim):
+    """Views of the float32 partials a split call left in its workspace:
+    (o_part [S, nrows, d], lse_part [S, nrows])."""
+    S = plan.num_splits
+    o_bytes = (S * nrows * head_dim * 4 + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    o = f[:S * nrows * head_dim * 4].view(torch.float32).view(S, nrows, head_dim)
+    l = f[o_bytes:o_bytes + S * nrows * 4].view(torch.float32).view(S, nrows)
+    return o, l
+
+
+def check_paged_inputs(shape_args, block_table_host, cache_seqlens_host, num_pages):
+    """Host check of block_table / cache_seqlens ranges (numpy int32 arrays).
+    Returns (status_name, bad_batch)."""
+    import numpy as np
+    shape = _L.DecodeShape(*shape_args)
+    bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    sl = np.ascontiguousarray(cache_seqlens_host, dtype=np.int32)
+    bad = ctypes.c_int32(-1)
+    code = _L.load().attn_check_paged_inputs(ctypes.byref(shape),
+                                             bt.ctypes.data_as(ctypes.c_void_p),
+                                             sl.ctypes.data_as(ctypes.c_void_p),
+                                             int(num_pages), ctypes.byref(bad))
+    return _L.STATUS[code], bad.value

@@ -1,0 +1,401 @@
+// attn_api.cpp -- the C ABI (include/attn_decode.h): validation, planning,
+// launches.  Host code only; the kernels live in *_kernel.hip.
+#include "attn_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int kBlockM = 16;         // M tile of the pack rule (MFMA tile height)
+constexpr int kBlockN = 128;        // N tile of the "at most 4 blocks" split rule
+constexpr int kGranule = 16;        // split ranges are multiples of 16 keys
+constexpr int kMaxSplitsRule = 128; // candidate split counts tried by the rule
+constexpr int kMaxSplits = 1024;    // largest split count a caller may ask for
+constexpr int kDefaultCus = 256;    // one MI355X
+constexpr int kMaxRowsPerBlock = 8;
+constexpr int kMaxDevices = 64;
+
+thread_local attn_plan g_last_plan;
+thread_local bool g_have_last = false;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// lpnh.cn "pack_gqa 与 num_splits" article, section "pack_gqa 怎么选": row
+// efficiency (valid rows over rows rounded up to the M tile) with and without
+// packing, single-precision quotients, packing when the unpacked one is below
+// 0.9 of the packed one (compared in double, as the page's literal is).
+bool should_pack_gqa(bool varlen_q, int seqlen_q, int group, int block_m) {
+  if (varlen_q) return true;
+  const float nopack = float(seqlen_q) / float(round_up(seqlen_q, block_m));
+  const int64_t rows = int64_t(seqlen_q) * group;
+  const float pack = float(rows) / float(round_up(rows, block_m));
+  return nopack < 0.9 * pack;
+}
+
+// Same article, section "num_splits 怎么选": one split when the units fill
+// 80% of the compute units or the KV spans at most 4 N tiles; otherwise the
+// smallest split count whose last-wave efficiency n_waves / ceil(n_waves) is
+// within 85% of the best over 1 .. min(128, N tiles).
+int num_splits_rule(int64_t total_mblocks, int num_cus, int64_t num_n_blocks) {
+  if (total_mblocks >= 0.8 * num_cus) return 1;
+  if (num_n_blocks <= 4) return 1;
+  const int max_splits = int(num_n_blocks < kMaxSplitsRule ? num_n_blocks : kMaxSplitsRule);
+  float eff[kMaxSplitsRule + 1];
+  float best = 0.f;
+  for (int s = 1; s <= max_splits; ++s) {
+    const float n_waves = float(total_mblocks * s) / float(num_cus);
+    eff[s] = n_waves / std::ceil(n_waves);
+    if (eff[s] > best) best = eff[s];
+  }
+  for (int s = 1; s <= max_splits; ++s)
+    if (eff[s] >= 0.85 * best) return s;
+  return 1;
+}
+
+int rows_per_block_for(int rows) {
+  if (rows <= 1) return 1;
+  if (rows <= 2) return 2;
+  if (rows <= 4) return 4;
+  return kMaxRowsPerBlock;
+}
+
+// Shared planner.  `dense` always packs (the dense API has no pack switch).
+attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, int64_t max_seqlen_k,
+                      int num_splits, int pack_gqa, int num_cus, bool dense, attn_plan* out) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
+  if (pack_gqa < -1 || pack_gqa > 1) return ATTN_ERR_ARG;
+  if (num_cus < 0) return ATTN_ERR_ARG;
+  if (num_cus == 0) num_cus = kDefaultCus;
+  const int group = hq / hkv;
+  bool pack;
+  if (dense)
+    pack = true;
+  else if (pack_gqa < 0)
+    pack = should_pack_gqa(false, q_len, group, kBlockM);
+  else
+    pack = pack_gqa == 1;
+  int splits = num_splits;
+  if (splits == 0) {
+    const int64_t heads = pack ? hkv : hq;
+    const int64_t rows = pack ? int64_t(q_len) * group : q_len;
+    const int64_t total = batch * heads * ceil_div(rows, kBlockM);
+    splits = num_splits_rule(total, num_cus, ceil_div(max_seqlen_k, kBlockN));
+  }
+  if (splits > 1) pack = true;  // same article, section "常见坑点"
+
+  const int64_t rows_per_unit = pack ? int64_t(q_len) * group : q_len;
+  const int rpb = rows_per_block_for(int(rows_per_unit > kMaxRowsPerBlock ? kMaxRowsPerBlock
+                                                                           : rows_per_unit));
+  const int64_t row_blocks = ceil_div(rows_per_unit, rpb);
+  const int64_t unit_heads = pack ? hkv : hq;
+  const int64_t units = batch * unit_heads * row_blocks;
+  const int64_t grid = units * splits;
+  if (grid > INT32_MAX || rows_per_unit > INT32_MAX) return ATTN_ERR_SHAPE;
+  const int64_t nrows = batch * q_len * int64_t(hq);
+  int64_t ws = 0;
+  if (splits > 1)
+    ws = round_up(int64_t(splits) * nrows * head_dim * 4, 256) + round_up(int64_t(splits) * nrows * 4, 256);
+
+  std::memset(out, 0, sizeof(*out));
+  out->num_splits = splits;
+  out->pack_gqa = pack ? 1 : 0;
+  out->rows_per_unit = int(rows_per_unit);
+  out->rows_per_block = rpb;
+  out->row_blocks = int(row_blocks);
+  out->units = int(units > INT32_MAX ? INT32_MAX : units);
+  out->grid = int(grid);
+  out->split_granule = kGranule;
+  out->num_cus = num_cus;
+  out->combine = splits > 1 ? 1 : 0;
+  out->kernel = skv::split_variant_id({0, head_dim, rpb, !dense});
+  out->workspace_bytes = ws;
+  return ATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+attn_status check_decode_shape(const attn_decode_shape* s) {
+  if (!s) return ATTN_ERR_NULL;
+  if (s->batch < 0 || s->q_len <= 0 || s->num_heads_q <= 0 || s->num_heads_kv <= 0 ||
+      s->head_dim <= 0 || s->page_size <= 0 || s->max_pages_per_seq <= 0 || s->max_seqlen_k < 0)
+    return ATTN_ERR_SHAPE;
+  if (s->num_heads_q % s->num_heads_kv != 0) return ATTN_ERR_SHAPE;
+  if (int64_t(s->max_seqlen_k) > int64_t(s->max_pages_per_seq) * s->page_size) return ATTN_ERR_SHAPE;
+  if (s->dtype != ATTN_FP16 && s->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (s->page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status check_dense_shape(const attn_dense_shape* s) {
+  if (!s) return ATTN_ERR_NULL;
+  if (s->num_heads_q <= 0 || s->num_heads_kv <= 0 || s->q_len <= 0 || s->kv_len < 0 ||
+      s->head_dim <= 0)
+    return ATTN_ERR_SHAPE;
+  if (s->num_heads_q % s->num_heads_kv != 0) return ATTN_ERR_SHAPE;
+  if (s->dtype != ATTN_FP16 && s->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status check_scale(float scale) {
+  if (std::isnan(scale) || std::isinf(scale)) return ATTN_ERR_ARG;
+  return ATTN_OK;
+}
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 0;
+  g_cu_count[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+attn_status check_workspace(const attn_plan& plan, void* ws, size_t ws_bytes) {
+  if (plan.workspace_bytes == 0) return ATTN_OK;
+  if (!ws || ws_bytes < size_t(plan.workspace_bytes)) return ATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+// Launch the split kernel (and the combine when S > 1) for a planned call.
+attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dtype, int head_dim,
+                void* out, float* lse, void* ws, hipStream_t stream) {
+  const int S = plan.num_splits;
+  prm.num_splits = S;
+  prm.rows = plan.rows_per_unit;
+  prm.row_blocks = plan.row_blocks;
+  prm.heads_per_unit = plan.pack_gqa ? prm.group : 1;
+  prm.unit_heads = plan.pack_gqa ? prm.hkv : prm.hq;
+  prm.out = out;
+  prm.lse = lse;
+  if (S > 1) {
+    const int64_t o_bytes = round_up(int64_t(S) * prm.nrows * head_dim * 4, 256);
+    prm.o_part = static_cast<float*>(ws);
+    prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+  }
+  skv::SplitVariant var{dtype, head_dim, plan.rows_per_block, paged};
+  if (!skv::split_variant_supported(var)) return ATTN_ERR_UNSUPPORTED;
+  if (skv::launch_split(var, prm, plan.grid, stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (S > 1) {
+    skv::CombineParams c{};
+    c.o_part = prm.o_part;
+    c.lse_part = prm.lse_part;
+    c.out = out;
+    c.lse = lse;
+    c.num_splits = S;
+    c.nrows = prm.nrows;
+    c.head_dim = head_dim;
+    if (paged) {
+      c.q_len = prm.q_len;
+      c.heads = prm.hq;
+    } else {  // dense rows (hq, i): batch = Hq, heads = 1
+      c.q_len = prm.q_len;
+      c.heads = 1;
+    }
+    if (skv::launch_combine(dtype, c, stream) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  g_last_plan = plan;
+  g_have_last = true;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int pack_gqa,
+                             int num_cus, attn_plan* plan) {
+  if (!plan) return ATTN_ERR_NULL;
+  attn_status st = check_decode_shape(shape);
+  if (st != ATTN_OK) return st;
+  return make_plan(shape->batch, shape->q_len, shape->num_heads_q, shape->num_heads_kv,
+                   shape->head_dim, shape->max_seqlen_k, num_splits, pack_gqa, num_cus, false,
+                   plan);
+}
+
+attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,
+                            attn_plan* plan) {
+  if (!plan) return ATTN_ERR_NULL;
+  attn_status st = check_dense_shape(shape);
+  if (st != ATTN_OK) return st;
+  return make_plan(1, shape->q_len, shape->num_heads_q, shape->num_heads_kv, shape->head_dim,
+                   shape->kv_len, num_splits, -1, num_cus, true, plan);
+}
+
+attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* cache_seqlens, int num_splits, int pack_gqa,
+                            float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  attn_status st = check_decode_shape(shape);
+  if (st != ATTN_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(cache_seqlens, 4) || (lse && !aligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != ATTN_OK) return st;
+  attn_plan plan;
+  const int cus = device_cus();
+  if (cus <= 0) return ATTN_ERR_HIP;
+  st = make_plan(shape->batch, shape->q_len, shape->num_heads_q, shape->num_heads_kv,
+                 shape->head_dim, shape->max_seqlen_k, num_splits, pack_gqa, cus, false, &plan);
+  if (st != ATTN_OK) return st;
+  if ((st = check_workspace(plan, workspace, workspace_bytes)) != ATTN_OK) return st;
+  if (shape->batch == 0) {
+    g_last_plan = plan;
+    g_have_last = true;
+    return ATTN_OK;
+  }
+  const int D = shape->head_dim;
+  skv::SplitParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.batch = shape->batch;
+  p.q_len = shape->q_len;
+  p.hq = shape->num_heads_q;
+  p.hkv = shape->num_heads_kv;
+  p.group = p.hq / p.hkv;
+  p.page_size = shape->page_size;
+  p.max_pages = shape->max_pages_per_seq;
+  p.kv_len = 0;
+  p.nrows = shape->batch * shape->q_len * shape->num_heads_q;
+  p.n_sb = shape->q_len * shape->num_heads_q;
+  p.n_si = shape->num_heads_q;
+  p.n_sh = 1;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(D));
+  p.scale_log2 = scale * 1.4426950408889634074f;
+  return run(plan, p, true, shape->dtype, D, out, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+attn_status attn_dense_fwd(const attn_dense_shape* shape, const void* q, const void* k,
+                           const void* v, int num_splits, float softmax_scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_dense_shape(shape);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      (lse && !aligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != ATTN_OK) return st;
+  attn_plan plan;
+  const int cus = device_cus();
+  if (cus <= 0) return ATTN_ERR_HIP;
+  st = make_plan(1, shape->q_len, shape->num_heads_q, shape->num_heads_kv, shape->head_dim,
+                 shape->kv_len, num_splits, -1, cus, true, &plan);
+  if (st != ATTN_OK) return st;
+  if ((st = check_workspace(plan, workspace, workspace_bytes)) != ATTN_OK) return st;
+  const int D = shape->head_dim;
+  skv::SplitParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.batch = 1;
+  p.q_len = shape->q_len;
+  p.hq = shape->num_heads_q;
+  p.hkv = shape->num_heads_kv;
+  p.group = p.hq / p.hkv;
+  p.page_size = 16;
+  p.max_pages = 0;
+  p.kv_len = shape->kv_len;
+  p.nrows = shape->num_heads_q * shape->q_len;
+  p.n_sb = 0;
+  p.n_si = 1;
+  p.n_sh = shape->q_len;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(D));
+  p.scale_log2 = scale * 1.4426950408889634074f;
+  return run(plan, p, false, shape->dtype, D, out, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+attn_status attn_combine_fwd(int num_splits, int batch, int q_len, int num_heads, int head_dim,
+                             int dtype, const float* o_part, const float* lse_part, void* out,
+                             float* lse, void* stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
+  if (batch < 0 || q_len <= 0 || num_heads <= 0 || head_dim <= 0) return ATTN_ERR_SHAPE;
+  if (head_dim > 512) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_FP16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!o_part || !lse_part || !out) return ATTN_ERR_NULL;
+  if (!aligned(o_part, 4) || !aligned(lse_part, 4) || !aligned(out, 2) || (lse && !aligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  const int64_t nrows = int64_t(batch) * q_len * num_heads;
+  if (nrows > INT32_MAX / 4) return ATTN_ERR_SHAPE;
+  if (nrows == 0) return ATTN_OK;
+  skv::CombineParams c{};
+  c.o_part = o_part;
+  c.lse_part = lse_part;
+  c.out = out;
+  c.lse = lse;
+  c.num_splits = num_splits;
+  c.nrows = int(nrows);
+  c.head_dim = head_dim;
+  c.q_len = q_len;
+  c.heads = num_heads;
+  if (skv::launch_combine(dtype, c, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status attn_check_paged_inputs(const attn_decode_shape* shape,
+                                    const int32_t* block_table_host,
+                                    const int32_t* cache_seqlens_host, int64_t num_pages,
+                                    int32_t* bad_batch) {
+  attn_status st = check_decode_shape(shape);
+  if (st != ATTN_OK) return st;
+  if (!block_table_host || !cache_seqlens_host) return ATTN_ERR_NULL;
+  for (int b = 0; b < shape->batch; ++b) {
+    const int L = cache_seqlens_host[b];
+    bool bad = L < 0 || L > shape->max_seqlen_k;
+    const int64_t used = bad ? 0 : ceil_div(L, shape->page_size);
+    for (int64_t t = 0; t < used && !bad; ++t) {
+      const int32_t pg = block_table_host[int64_t(b) * shape->max_pages_per_seq + t];
+      bad = pg < 0 || pg >= num_pages;
+    }
+    if (bad) {
+      if (bad_batch) *bad_batch = b;
+      return ATTN_ERR_DATA;
+    }
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_last_plan(attn_plan* plan) {
+  if (!plan) return ATTN_ERR_NULL;
+  if (!g_have_last) return ATTN_ERR_ARG;
+  *plan = g_last_plan;
+  return ATTN_OK;
+}
+
+const char* attn_status_str(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "inconsistent sizes";
+    case ATTN_ERR_UNSUPPORTED: return "outside the supported envelope";
+    case ATTN_ERR_ARG: return "argument out of range";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_DATA: return "block_table or cache_seqlens entry out of range";
+  }
+  return "unknown status";
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

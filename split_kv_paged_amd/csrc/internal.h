@@ -1,0 +1,64 @@
+// internal.h -- launch parameters shared by the host API and the HIP kernels.
+// Not part of the public ABI (include/attn_decode.h is).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+// One split-kernel launch.  Rows: a "row" is one (b, i, hq) query vector.
+//   row index n(b, i, hq) = b * n_sb + i * n_si + hq * n_sh
+//   q / out element offset = n * head_dim          (both layouts)
+//   lse index              = (b * Hq + hq) * q_len + i
+// KV addressing of key t, KV head h:
+//   paged: page = block_table[b * max_pages + t / page_size],
+//          elem = ((page * page_size + t % page_size) * Hkv + h) * head_dim
+//   dense: elem = (h * kv_len + t) * head_dim
+struct SplitParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;  // paged only
+  const int32_t* seqlens;      // paged only
+  void* out;                   // final output (num_splits == 1)
+  float* lse;                  // final LSE, may be null (num_splits == 1)
+  float* o_part;               // [S][nrows][D] (num_splits > 1)
+  float* lse_part;             // [S][nrows]    (num_splits > 1)
+  int batch, q_len, hq, hkv, group;  // group = Hq / Hkv
+  int page_size, max_pages, kv_len;
+  int num_splits;
+  int rows;            // valid rows per unit (q_len * heads_per_unit)
+  int row_blocks;      // ceil(rows / R)
+  int heads_per_unit;  // group (packed) or 1
+  int unit_heads;      // Hkv (packed) or Hq
+  int nrows;           // batch * q_len * Hq
+  int n_sb, n_si, n_sh;
+  float scale_log2;    // softmax scale * log2(e)
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  void* out;
+  float* lse;          // may be null
+  int num_splits;
+  int nrows;
+  int head_dim;
+  // row n = (b * q_len + i) * heads + h  ->  lse index (b * heads + h) * q_len + i
+  int q_len, heads;
+};
+
+// Kernel variant selector: dtype (0 fp16, 1 bf16), head_dim, rows per block.
+struct SplitVariant {
+  int dtype;
+  int head_dim;
+  int rows_per_block;
+  bool paged;
+};
+
+hipError_t launch_split(const SplitVariant& v, const SplitParams& p, int grid, hipStream_t s);
+hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t s);
+bool split_variant_supported(const SplitVariant& v);
+int split_variant_id(const SplitVariant& v);
+
+}  // namespace skv

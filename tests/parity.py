@@ -1,0 +1,81 @@
+"""Comparison helpers for GPU-vs-oracle parity (no attention arithmetic here).
+
+Tolerances (the bar for every parity test):
+  * outputs in fp16: |gpu - oracle| <= 2e-3 + ulp_fp16(|oracle|)
+  * outputs in bf16: |gpu - oracle| <= 1e-2 + ulp_bf16(|oracle|)
+  * LSE (float32):  |gpu - oracle| <= 1e-3
+  * float32 partial outputs (before the final rounding): <= 1e-3
+The ulp term is the spacing of the output type at the exact value: rounding
+the exact result to fp16/bf16 alone moves it by up to half of that, which
+exceeds the absolute bound wherever |O| >= 8 (fp16) or >= 4 (bf16).
+Rows with no keys must be exactly O = 0, LSE = -inf.
+"""
+import numpy as np
+import torch
+
+from split_kv_paged_amd import workloads as W
+
+ATOL = {"fp16": 2e-3, "bf16": 1e-2}
+LSE_ATOL = 1e-3
+PART_ATOL = 1e-3
+TORCH_DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to_dev(bits, dtype, device="cuda"):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(TORCH_DT[dtype]).to(device)
+
+
+def i32_dev(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def bits_of(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp(x, dtype):
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    if dtype == "fp16":
+        a16 = np.minimum(a, 65504.0).astype(np.float16)
+        return np.spacing(a16).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_out(got_bits, ref, dtype, what="out"):
+    got = W.from_bits(got_bits, dtype).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s: non-finite output" % what
+    err = np.abs(got - ref)
+    allow = ATOL[dtype] + ulp(ref, dtype)
+    bad = err > allow
+    if bad.any():
+        idx = np.unravel_index(np.argmax(err - allow), err.shape)
+        raise AssertionError("%s: %d/%d elements out of tolerance; worst at %s: gpu %r oracle %r "
+                             "(max abs err %.3g)" % (what, bad.sum(), err.size, idx, got[idx],
+                                                     ref[idx], err.max()))
+    return float(err.max()) if err.size else 0.0
+
+
+def check_lse(got, ref, what="lse", atol=LSE_ATOL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    empty = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), empty), "%s: -inf pattern differs" % what
+    if (~empty).any():
+        err = np.abs(got[~empty] - ref[~empty])
+        assert err.max() <= atol, "%s: max err %.3g" % (what, err.max())
+        return float(err.max())
+    return 0.0
+
+
+def check_f32(got, ref, atol=PART_ATOL, what="partial"):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), what
+    assert err.max(initial=0.0) <= atol, "%s: max err %.3g" % (what, err.max())
+    return float(err.max(initial=0.0))

@@ -1,0 +1,199 @@
+"""Host-only checks of the C-ABI library: it loads, exports every symbol the
+header declares, plans like the oracle planner, and rejects bad arguments
+before touching any device (no compute call is made here)."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import planner as oplan
+from split_kv_paged_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from split_kv_paged_amd import build
+        build.build()
+    return L.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = header_functions()
+    assert set(declared) == set(L.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = os.popen("nm -D --defined-only %s" % L.LIB_PATH).read()
+    for name in declared:
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define ATTN_ABI_VERSION (\d+)", text).group(1))
+    assert lib.attn_abi_version() == v
+
+
+def test_status_strings(lib):
+    for code in L.STATUS:
+        assert lib.attn_status_str(code)
+    assert lib.attn_status_str(99) == b"unknown status"
+
+
+def _plan(lib, **kw):
+    shape = L.DecodeShape(kw["batch"], kw["q_len"], kw["hq"], kw["hkv"], kw.get("d", 128),
+                          kw.get("page", 16), kw.get("maxp", 64), kw["max_L"], kw.get("dt", 1))
+    plan = L.Plan()
+    code = lib.attn_decode_plan(ctypes.byref(shape), kw.get("S", 0), kw.get("pack", -1),
+                                kw.get("cus", 0), ctypes.byref(plan))
+    return code, plan
+
+
+PLAN_GRID = list(itertools.product([1, 2, 3, 4, 7, 13, 32, 128], [1, 2, 4, 8], [1, 2, 3, 4, 8],
+                                   [1, 2, 4, 8], [1, 100, 513, 1024, 4096, 16384],
+                                   [0, 1, 4], [-1, 0, 1]))
+
+
+def test_plan_matches_oracle_planner(lib):
+    """Bit-exact parity of the host planning step with the oracle planner,
+    over a grid of batch x qLen x G x Hkv x max_seqlen_k x splits x pack."""
+    n = 0
+    for batch, q_len, G, hkv, max_L, S, pack in PLAN_GRID:
+        hq = G * hkv
+        maxp = (max_L + 15) // 16
+        code, plan = _plan(lib, batch=batch, q_len=q_len, hq=hq, hkv=hkv, max_L=max_L,
+                           maxp=maxp, S=S, pack=pack)
+        assert code == 0
+        want = oplan.plan(batch, q_len, hq, hkv, max_L, 256, 16, 128, S, pack)
+        assert (plan.num_splits, bool(plan.pack_gqa)) == want, (batch, q_len, G, hkv, max_L, S,
+                                                                 pack)
+        n += 1
+    assert n == len(PLAN_GRID)
+
+
+@pytest.mark.parametrize("cus", [80, 132, 304])
+def test_plan_uses_given_cu_count(lib, cus):
+    for batch, hkv, max_L in [(1, 1, 8192), (2, 4, 16384), (5, 8, 3000), (64, 8, 1024)]:
+        code, plan = _plan(lib, batch=batch, q_len=1, hq=4 * hkv, hkv=hkv, max_L=max_L,
+                           maxp=(max_L + 15) // 16, cus=cus)
+        assert code == 0
+        assert plan.num_cus == cus
+        assert (plan.num_splits, bool(plan.pack_gqa)) == oplan.plan(batch, 1, 4 * hkv, hkv,
+                                                                    max_L, cus, 16, 128, 0, -1)
+
+
+def test_plan_fields_are_consistent(lib):
+    code, plan = _plan(lib, batch=4, q_len=1, hq=32, hkv=4, max_L=16384, maxp=1024)
+    assert code == 0
+    assert plan.num_splits == 14 and plan.pack_gqa == 1
+    assert plan.rows_per_unit == 8 and plan.rows_per_block == 8 and plan.row_blocks == 1
+    assert plan.units == 4 * 4 and plan.grid == 16 * 14 and plan.combine == 1
+    nrows = 4 * 1 * 32
+    o = (14 * nrows * 128 * 4 + 255) // 256 * 256
+    assert plan.workspace_bytes == o + (14 * nrows * 4 + 255) // 256 * 256
+    # the target paged decode workload: packed, one split, no workspace
+    code, plan = _plan(lib, batch=32, q_len=1, hq=32, hkv=8, max_L=1100, maxp=69)
+    assert (plan.num_splits, plan.pack_gqa, plan.rows_per_block, plan.grid) == (1, 1, 4, 256)
+    assert plan.workspace_bytes == 0 and plan.combine == 0
+    # rows beyond 8 go to row blocks
+    code, plan = _plan(lib, batch=2, q_len=3, hq=32, hkv=4, max_L=512, maxp=32, S=1, pack=1)
+    assert plan.rows_per_unit == 24 and plan.rows_per_block == 8 and plan.row_blocks == 3
+    # unpacked: one query head per unit
+    code, plan = _plan(lib, batch=2, q_len=2, hq=8, hkv=2, max_L=512, maxp=32, S=1, pack=0)
+    assert plan.rows_per_unit == 2 and plan.units == 2 * 8
+
+
+@pytest.mark.parametrize("field,value,want", [
+    ("batch", -1, "ATTN_ERR_SHAPE"), ("q_len", 0, "ATTN_ERR_SHAPE"),
+    ("hq", 0, "ATTN_ERR_SHAPE"), ("hkv", 3, "ATTN_ERR_SHAPE"),
+    ("d", 96, "ATTN_ERR_UNSUPPORTED"), ("d", 0, "ATTN_ERR_SHAPE"),
+    ("page", 0, "ATTN_ERR_SHAPE"), ("page", 8, "ATTN_ERR_UNSUPPORTED"),
+    ("maxp", 0, "ATTN_ERR_SHAPE"), ("max_L", 8193, "ATTN_ERR_SHAPE"),
+    ("max_L", -5, "ATTN_ERR_SHAPE"), ("dt", 2, "ATTN_ERR_UNSUPPORTED"),
+    ("S", -1, "ATTN_ERR_ARG"), ("S", 1025, "ATTN_ERR_ARG"), ("pack", 2, "ATTN_ERR_ARG"),
+    ("pack", -2, "ATTN_ERR_ARG"), ("cus", -1, "ATTN_ERR_ARG"),
+])
+def test_plan_rejects(lib, field, value, want):
+    kw = dict(batch=2, q_len=1, hq=8, hkv=2, d=128, page=16, maxp=512, max_L=4096)
+    kw[field] = value
+    code, _ = _plan(lib, **kw)
+    assert L.STATUS[code] == want
+
+
+def test_plan_null_arguments(lib):
+    plan = L.Plan()
+    assert L.STATUS[lib.attn_decode_plan(None, 0, -1, 0, ctypes.byref(plan))] == "ATTN_ERR_NULL"
+    shape = L.DecodeShape(1, 1, 8, 2, 128, 16, 4, 64, 1)
+    assert L.STATUS[lib.attn_decode_plan(ctypes.byref(shape), 0, -1, 0, None)] == "ATTN_ERR_NULL"
+
+
+def test_dense_plan(lib):
+    plan = L.Plan()
+    shape = L.DenseShape(32, 32, 4, 4096, 128, 0)
+    assert lib.attn_dense_plan(ctypes.byref(shape), 0, 0, ctypes.byref(plan)) == 0
+    assert plan.num_splits == oplan.plan(1, 4, 32, 32, 4096, 256, 16, 128, 0, 1)[0] == 7
+    shape = L.DenseShape(8, 2, 1, 512, 64, 0)
+    assert lib.attn_dense_plan(ctypes.byref(shape), 0, 0, ctypes.byref(plan)) == 0
+    assert plan.num_splits == 1 and plan.rows_per_unit == 4
+    for bad, want in [(L.DenseShape(8, 3, 1, 512, 64, 0), "ATTN_ERR_SHAPE"),
+                      (L.DenseShape(8, 2, 0, 512, 64, 0), "ATTN_ERR_SHAPE"),
+                      (L.DenseShape(8, 2, 1, -1, 64, 0), "ATTN_ERR_SHAPE"),
+                      (L.DenseShape(8, 2, 1, 512, 80, 0), "ATTN_ERR_UNSUPPORTED")]:
+        assert L.STATUS[lib.attn_dense_plan(ctypes.byref(bad), 0, 0, ctypes.byref(plan))] == want
+
+
+def test_forward_validation_before_any_device_call(lib):
+    """Argument errors return before the library touches HIP."""
+    P = ctypes.c_void_p
+    good = L.DecodeShape(2, 1, 8, 2, 128, 16, 4, 64, 1)
+    a = P(0x10000)  # never dereferenced: every call below fails validation first
+    assert L.STATUS[lib.attn_decode_fwd(None, a, a, a, a, a, 0, -1, 0.0, a, None, None, 0,
+                                        None)] == "ATTN_ERR_NULL"
+    assert L.STATUS[lib.attn_decode_fwd(ctypes.byref(good), None, a, a, a, a, 0, -1, 0.0, a,
+                                        None, None, 0, None)] == "ATTN_ERR_NULL"
+    bad = L.DecodeShape(2, 1, 8, 3, 128, 16, 4, 64, 1)
+    assert L.STATUS[lib.attn_decode_fwd(ctypes.byref(bad), a, a, a, a, a, 0, -1, 0.0, a, None,
+                                        None, 0, None)] == "ATTN_ERR_SHAPE"
+    odd = P(0x10002)
+    assert L.STATUS[lib.attn_decode_fwd(ctypes.byref(good), odd, a, a, a, a, 0, -1, 0.0, a,
+                                        None, None, 0, None)] == "ATTN_ERR_ALIGN"
+    assert L.STATUS[lib.attn_decode_fwd(ctypes.byref(good), a, a, a, a, a, 0, -1,
+                                        float("nan"), a, None, None, 0, None)] == "ATTN_ERR_ARG"
+    dshape = L.DenseShape(8, 2, 1, 512, 96, 0)
+    assert L.STATUS[lib.attn_dense_fwd(ctypes.byref(dshape), a, a, a, 0, 0.0, a, None, None, 0,
+                                       None)] == "ATTN_ERR_UNSUPPORTED"
+    assert L.STATUS[lib.attn_combine_fwd(0, 1, 1, 8, 128, 1, a, a, a, None, None)] == \
+        "ATTN_ERR_ARG"
+    assert L.STATUS[lib.attn_combine_fwd(2, 1, 1, 8, 513, 1, a, a, a, None, None)] == \
+        "ATTN_ERR_UNSUPPORTED"
+    assert L.STATUS[lib.attn_combine_fwd(2, 1, 1, 8, 128, 1, None, a, a, None, None)] == \
+        "ATTN_ERR_NULL"
+
+
+def test_check_paged_inputs(lib):
+    from split_kv_paged_amd import api
+    bt = np.array([[0, 1, 2, 3], [4, 5, 6, 99]], dtype=np.int32)
+    args = (2, 1, 8, 2, 128, 16, 4, 64, 1)
+    assert api.check_paged_inputs(args, bt, np.array([64, 48], np.int32), 7) == ("ATTN_OK", -1)
+    assert api.check_paged_inputs(args, bt, np.array([64, 49], np.int32), 7) == \
+        ("ATTN_ERR_DATA", 1)
+    assert api.check_paged_inputs(args, bt, np.array([65, 1], np.int32), 7) == \
+        ("ATTN_ERR_DATA", 0)
+    assert api.check_paged_inputs(args, bt, np.array([-1, 1], np.int32), 7) == \
+        ("ATTN_ERR_DATA", 0)
+    bt[0, 0] = -3
+    assert api.check_paged_inputs(args, bt, np.array([1, 0], np.int32), 7) == \
+        ("ATTN_ERR_DATA", 0)
+    assert api.check_paged_inputs(args, bt, np.array([0, 0], np.int32), 7) == ("ATTN_OK", -1)

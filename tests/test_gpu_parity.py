@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Every test prints the case it is about to run (flushed) before its first
+GPU call.  Full-size cases use the five named workloads; small cases span
+several 16-key tiles with ragged tails, GQA 1/2/4/8, q_len up to 8 (row
+blocks), head_dim 64/128, both dtypes, page sizes 16/32, empty sequences
+and NaN-poisoned slots outside the valid keys.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from split_kv_paged_amd import api
+from split_kv_paged_amd import workloads as W
+from tests.parity import (bits_of, check_f32, check_lse, check_out, i32_dev, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def case(msg):
+    print("\n[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_paged(wl, num_splits=0, pack_gqa=-1, workspace=None):
+    q = to_dev(wl.q, wl.dtype)
+    kc = to_dev(wl.k_cache, wl.dtype)
+    vc = to_dev(wl.v_cache, wl.dtype)
+    bt = i32_dev(wl.block_table)
+    sl = i32_dev(wl.cache_seqlens)
+    out, lse = api.decode_fwd(q, kc, vc, bt, sl, num_splits=num_splits, pack_gqa=pack_gqa,
+                              softmax_scale=wl.scale, max_seqlen_k=max(wl.max_seqlen_k, 0),
+                              workspace=workspace)
+    torch.cuda.synchronize()
+    return bits_of(out), lse.cpu().numpy(), api.last_plan()
+
+
+def oracle_paged(wl):
+    return oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                  wl.cache_seqlens, wl.dtype, scale=wl.scale)
+
+
+def assert_paged(wl, num_splits=0, pack_gqa=-1, ref=None):
+    ref_o, ref_l = ref if ref is not None else oracle_paged(wl)
+    out, lse, plan = run_paged(wl, num_splits, pack_gqa)
+    e1 = check_out(out, ref_o, wl.dtype, "%s S=%d" % (wl.name, num_splits))
+    e2 = check_lse(lse, ref_l)
+    print("  plan S=%d pack=%d rows/blk=%d grid=%d  max|dO|=%.3g max|dLSE|=%.3g" % (
+        plan.num_splits, plan.pack_gqa, plan.rows_per_block, plan.grid, e1, e2), flush=True)
+    return plan
+
+
+# ---------------------------------------------------------------- workloads --
+
+@pytest.fixture(scope="module")
+def c3():
+    wl = W.c3_paged_gqa4()
+    return wl, oracle_paged(wl)
+
+
+def test_paged_gqa4_bf16_full_size_planner(c3):
+    wl, ref = c3
+    case("paged bf16 B32 Hq32/Hkv8 d128 L~U[900,1100], planner splits")
+    plan = assert_paged(wl, ref=ref)
+    assert plan.num_splits == 1 and plan.pack_gqa == 1
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 8])
+def test_paged_gqa4_bf16_full_size_split_sweep(c3, S):
+    wl, ref = c3
+    case("paged bf16 B32 Hq32/Hkv8 d128, num_splits=%d" % S)
+    plan = assert_paged(wl, num_splits=S, ref=ref)
+    assert plan.num_splits == S and plan.combine == 1
+
+
+def test_paged_gqa4_bf16_full_size_unpacked(c3):
+    wl, ref = c3
+    case("paged bf16 B32 Hq32/Hkv8 d128, pack_gqa=0")
+    plan = assert_paged(wl, num_splits=1, pack_gqa=0, ref=ref)
+    assert plan.pack_gqa == 0 and plan.rows_per_unit == 1
+
+
+@pytest.fixture(scope="module")
+def c4():
+    wl = W.c4_long()
+    return wl, oracle_paged(wl)
+
+
+@pytest.mark.parametrize("S", [0, 1, 2, 4, 8, 16])
+def test_long_context_bf16_split_sweep(c4, S):
+    wl, ref = c4
+    case("paged bf16 B4 Hq32/Hkv4 d128 L16384, num_splits=%d" % S)
+    plan = assert_paged(wl, num_splits=S, ref=ref)
+    if S == 0:
+        assert plan.num_splits == 14
+
+
+def test_ragged_fp16_outliers_full_size():
+    wl = W.c5_ragged()
+    case("paged fp16 B128 Hq16/Hkv8 d64 L log-uniform 1..8192, 1%% outliers x8 (%d rows)"
+         % wl.meta["outlier_rows"])
+    ref = oracle_paged(wl)
+    assert_paged(wl, ref=ref)
+    case("same, num_splits=8")
+    assert_paged(wl, num_splits=8, ref=ref)
+
+
+def test_dense_decode_fp16():
+    wl = W.c1_dense_decode()
+    case("dense fp16 Hq8/Hkv2 d64 kvLen512 scale 1/8, num_splits=1")
+    ref_o, ref_l = oracle.dense_attention(wl.q, wl.k, wl.v, "fp16", scale=wl.scale)
+    out, lse = api.dense_fwd(to_dev(wl.q, "fp16"), to_dev(wl.k, "fp16"), to_dev(wl.v, "fp16"),
+                             num_splits=1, softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    check_out(bits_of(out), ref_o, "fp16")
+    check_lse(lse.cpu().numpy(), ref_l)
+    assert api.last_plan().num_splits == 1
+
+
+@pytest.mark.parametrize("kv_len", W.C2_KV_LENS)
+def test_smallq_mha_fp16(kv_len):
+    wl = W.c2_smallq(kv_len)
+    case("dense fp16 MHA 32 heads qLen4 d128 kvLen=%d, planner splits" % kv_len)
+    ref_o, ref_l = oracle.dense_attention(wl.q, wl.k, wl.v, "fp16")
+    q, k, v = to_dev(wl.q, "fp16"), to_dev(wl.k, "fp16"), to_dev(wl.v, "fp16")
+    out, lse = api.dense_fwd(q, k, v)
+    torch.cuda.synchronize()
+    plan = api.last_plan()
+    check_out(bits_of(out), ref_o, "fp16")
+    check_lse(lse.cpu().numpy(), ref_l)
+    if kv_len == 1:  # one key: O is that value row, exactly
+        np.testing.assert_array_equal(bits_of(out), np.broadcast_to(wl.v, out.shape))
+    for S in (1, 3):
+        case("dense fp16 MHA kvLen=%d num_splits=%d" % (kv_len, S))
+        out, lse = api.dense_fwd(q, k, v, num_splits=S)
+        torch.cuda.synchronize()
+        check_out(bits_of(out), ref_o, "fp16")
+        check_lse(lse.cpu().numpy(), ref_l)
+    print("  planner S=%d" % plan.num_splits, flush=True)
+
+
+# ------------------------------------------------------------- small shapes --
+
+SMALL = [
+    # dtype, B, qlen, Hq, Hkv, d, page, lens
+    ("bf16", 3, 1, 8, 2, 128, 16, [1, 17, 100]),
+    ("fp16", 3, 1, 8, 2, 128, 16, [15, 16, 33]),
+    ("bf16", 2, 1, 16, 2, 64, 16, [250, 7]),
+    ("fp16", 4, 1, 4, 4, 64, 32, [31, 32, 33, 95]),
+    ("bf16", 2, 2, 8, 2, 128, 16, [40, 129]),      # qlen 2, G 4: 8 rows
+    ("fp16", 2, 3, 8, 4, 64, 16, [77, 3]),          # 6 rows -> R 8 with 2 idle rows
+    ("bf16", 2, 4, 16, 4, 128, 32, [200, 64]),      # 16 rows -> 2 row blocks
+    ("fp16", 1, 8, 8, 1, 128, 16, [300]),           # 64 rows -> 8 row blocks, MQA
+    ("bf16", 5, 1, 8, 8, 128, 16, [1, 2, 3, 16, 17]),  # MHA
+    ("fp16", 2, 1, 24, 3, 64, 48, [500, 1000]),     # G 8, page 48
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: "%s-B%d-q%d-%dx%d-d%d-p%d" % s[:7])
+@pytest.mark.parametrize("S", [0, 1, 2, 5])
+def test_small_paged_shapes(spec, S):
+    dt, B, qlen, hq, hkv, d, page, lens = spec
+    wl = W.make_paged(700 + B * 10 + d + qlen, dt, B, qlen, hq, hkv, d, page, lens,
+                      spare_pages=2, outlier_p=0.02)
+    case("small paged %s S=%d" % (str(spec), S))
+    ref = oracle_paged(wl)
+    assert_paged(wl, num_splits=S, ref=ref)
+    if S == 1:
+        case("small paged %s S=1 pack_gqa=0" % str(spec))
+        assert_paged(wl, num_splits=1, pack_gqa=0, ref=ref)
+
+
+def test_empty_sequences_and_zero_batch():
+    wl = W.make_paged(801, "bf16", 4, 1, 8, 2, 128, 16, [0, 20, 0, 1], spare_pages=2)
+    for S in (1, 3):
+        case("empty sequences (L=0) among others, S=%d" % S)
+        out, lse, _ = run_paged(wl, num_splits=S)
+        ref_o, ref_l = oracle_paged(wl)
+        check_out(out, ref_o, "bf16")
+        check_lse(lse, ref_l)
+        assert np.all(W.from_bits(out[0], "bf16") == 0) and np.all(np.isneginf(lse[0]))
+    case("all sequences empty")
+    wl0 = W.make_paged(802, "fp16", 2, 1, 4, 2, 64, 16, [0, 0], spare_pages=1)
+    out, lse, _ = run_paged(wl0)
+    assert np.all(W.from_bits(out, "fp16") == 0) and np.all(np.isneginf(lse))
+
+
+def test_partials_and_combine_separately():
+    """Rows a9 and a10 on their own: the split kernel's float32 partials
+    against the oracle's per-split online recurrence, then the combine
+    kernel fed with the oracle's partials."""
+    wl = W.make_paged(811, "bf16", 3, 2, 8, 2, 128, 16, [1, 200, 517], spare_pages=2)
+    S = 4
+    plan = api.decode_plan(3, 2, 8, 2, 128, 16, wl.block_table.shape[1], wl.max_seqlen_k,
+                           torch.bfloat16, num_splits=S)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    case("split partials S=4 read back from the workspace")
+    run_paged(wl, num_splits=S, workspace=ws)
+    nrows = 3 * 2 * 8
+    o_gpu, l_gpu = api.workspace_partials(ws, plan, nrows, 128)
+    o_ref, l_ref = oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                               wl.cache_seqlens, "bf16", S, 16, block=16,
+                                               scale=wl.scale)
+    check_f32(o_gpu.cpu().numpy(), o_ref)
+    check_lse(l_gpu.cpu().numpy(), l_ref)
+    case("combine kernel on the oracle's partials")
+    o32 = o_ref.astype(np.float32)
+    l32 = l_ref.astype(np.float32)
+    out, lse = api.combine_fwd(torch.from_numpy(o32).cuda(), torch.from_numpy(l32).cuda(), 3, 2,
+                               8, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.combine(o32.astype(np.float64), l32.astype(np.float64))
+    check_out(bits_of(out).reshape(nrows, 128), ref_o, "bf16")
+    check_lse(lse.cpu().numpy().transpose(0, 2, 1).reshape(nrows), ref_l)
+
+
+@pytest.mark.parametrize("d", [1, 5, 64, 200, 512])
+def test_combine_any_head_dim(d):
+    rng = np.random.default_rng(d)
+    S, B, qlen, H = 5, 2, 3, 4
+    n = B * qlen * H
+    o = rng.standard_normal((S, n, d)).astype(np.float32)
+    l = (3 * rng.standard_normal((S, n))).astype(np.float32)
+    l[1, :4] = -np.inf
+    l[:, 5] = -np.inf  # row 5: every partial empty
+    o[:, 5] = 0
+    case("combine S=5 head_dim=%d" % d)
+    out, lse = api.combine_fwd(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), B, qlen,
+                               H, dtype=torch.float16)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.combine(o.astype(np.float64), l.astype(np.float64))
+    check_out(bits_of(out).reshape(n, d), ref_o, "fp16")
+    check_lse(lse.cpu().numpy().transpose(0, 2, 1).reshape(n), ref_l)
+
+
+def test_bitwise_determinism_and_page_permutation():
+    wl = W.make_paged(821, "bf16", 4, 1, 32, 8, 128, 16, [300, 1000, 17, 640], spare_pages=3)
+    case("determinism: two runs bitwise equal, S=1 and S=4")
+    for S in (1, 4):
+        a, la, _ = run_paged(wl, num_splits=S)
+        b, lb, _ = run_paged(wl, num_splits=S)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+    case("physical page permutation leaves the output bitwise unchanged")
+    rng = np.random.default_rng(5)
+    n = wl.k_cache.shape[0]
+    perm = rng.permutation(n)
+    kc = np.empty_like(wl.k_cache); vc = np.empty_like(wl.v_cache)
+    kc[perm] = wl.k_cache; vc[perm] = wl.v_cache
+    wl2 = W.PagedWorkload(**{**wl.__dict__, "k_cache": kc, "v_cache": vc,
+                             "block_table": perm[wl.block_table].astype(np.int32)})
+    for S in (1, 4):
+        a, la, _ = run_paged(wl, num_splits=S)
+        b, lb, _ = run_paged(wl2, num_splits=S)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_last_plan_matches_host_plan():
+    wl = W.c4_long()
+    case("last_plan after a forward equals the host plan (long context, planner)")
+    run_paged(wl)
+    got = api.last_plan().as_dict()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    want = api.decode_plan(4, 1, 32, 4, 128, 16, wl.block_table.shape[1], wl.max_seqlen_k,
+                           torch.bfloat16, num_cus=cus).as_dict()
+    assert got == want
+    print("  device CUs=%d plan=%s" % (cus, got), flush=True)
+
+
+def test_workspace_too_small_is_rejected_and_writes_nothing():
+    wl = W.make_paged(831, "fp16", 2, 1, 8, 2, 64, 16, [100, 200], spare_pages=1)
+    q = to_dev(wl.q, "fp16")
+    out = torch.full_like(q, 7.0)
+    ws = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    case("workspace too small for S=3")
+    with pytest.raises(Exception) as ei:
+        api.decode_fwd(q, to_dev(wl.k_cache, "fp16"), to_dev(wl.v_cache, "fp16"),
+                       i32_dev(wl.block_table), i32_dev(wl.cache_seqlens), num_splits=3,
+                       out=out, workspace=ws)
+    assert "ATTN_ERR_WORKSPACE" in str(ei.value)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_scale_override():
+    wl = W.make_paged(841, "bf16", 2, 1, 8, 2, 128, 16, [60, 90], spare_pages=1, scale=0.37)
+    case("softmax_scale=0.37")
+    assert_paged(wl)
