@@ -113,11 +113,12 @@ typedef struct {
     int32_t row_blocks;      /* ceil(rows_per_unit / rows_per_block)           */
     int32_t units;           /* batch * head units * row_blocks               */
     int32_t grid;            /* workgroups of the split kernel = units * S    */
-    int32_t split_granule;   /* split ranges are multiples of this many keys   */
+    int32_t split_granule;   /* split lengths are multiples of this many keys  */
     int32_t num_cus;         /* compute units the plan was made for           */
     int32_t combine;         /* 1 when a combine pass merges S > 1 partials   */
     int32_t kernel;          /* kernel variant id (diagnostic)                */
-    int32_t reserved;
+    int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
+                             /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
     int64_t workspace_bytes; /* bytes of workspace the forward call needs     */
 } attn_plan;
 

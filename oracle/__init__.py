@@ -174,12 +174,19 @@ def dense_attention(q, k, v, dtype, scale=None, nthreads=None):
     return out, lse
 
 
+def split_keys_for(max_len, num_splits, granule=16):
+    """One split length for a batch: C = granule * ceil(ceil(max_len/granule)/S)
+    (at least one granule)."""
+    units = -(-max(int(max_len), 0) // granule)
+    return granule * max(1, -(-units // num_splits))
+
+
 def paged_split_partials(q, k_cache, v_cache, block_table, cache_seqlens, dtype, num_splits,
-                         granule, block=16, scale=None, nthreads=None):
+                         split_keys, block=16, scale=None, nthreads=None):
     """Per-split partials via the online-softmax recurrence (float64).
 
-    Split s of a sequence with L keys covers keys [s*T*granule, (s+1)*T*granule)
-    clipped to L, T = ceil(ceil(L/granule)/S).  Returns
+    Split s of a sequence with L keys covers keys [s*C, (s+1)*C) clipped to
+    [0, L), C = split_keys (S*C must reach every L).  Returns
     (o_part [S, B*qlen*Hq, d], lse_part [S, B*qlen*Hq]) with rows
     n = (b*qlen + i)*Hq + hq; empty splits give zeros and -inf.
     """
@@ -195,14 +202,14 @@ def paged_split_partials(q, k_cache, v_cache, block_table, cache_seqlens, dtype,
     l = np.zeros((num_splits, n), dtype=np.float64)
     rc = lib.oracle_paged_split_partials(B, qlen, hq, hkv, d, page, bt.shape[1], _dt(dtype),
                                          _p(q), _p(kc), _p(vc), _p(bt), _p(sl), float(scale),
-                                         num_splits, granule, block,
+                                         num_splits, split_keys, block,
                                          nthreads or default_threads(), _p(o), _p(l))
     if rc != 0:
         raise ValueError("oracle_paged_split_partials rejected the shape")
     return o, l
 
 
-def dense_split_partials(q, k, v, dtype, num_splits, granule, block=16, scale=None,
+def dense_split_partials(q, k, v, dtype, num_splits, split_keys, block=16, scale=None,
                          nthreads=None):
     """Dense-layout counterpart of paged_split_partials; rows n = hq*qlen + i."""
     lib = _load()
@@ -215,7 +222,7 @@ def dense_split_partials(q, k, v, dtype, num_splits, granule, block=16, scale=No
     o = np.zeros((num_splits, n, d), dtype=np.float64)
     l = np.zeros((num_splits, n), dtype=np.float64)
     rc = lib.oracle_dense_split_partials(hq, hkv, qlen, kvlen, d, _dt(dtype), _p(q), _p(k), _p(v),
-                                         float(scale), num_splits, granule, block,
+                                         float(scale), num_splits, split_keys, block,
                                          nthreads or default_threads(), _p(o), _p(l))
     if rc != 0:
         raise ValueError("oracle_dense_split_partials rejected the shape")

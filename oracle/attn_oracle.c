@@ -36,8 +36,9 @@
  *
  *   Readings where the pages are silent (each also listed in the design
  *   notes): natural-log LSE in units of scaled scores; L = 0 gives O = 0 and
- *   LSE = -inf; head mapping h = hq / G; split ranges are contiguous runs of
- *   `granule`-token units, T = ceil(units / S) per split, empty splits give
+ *   LSE = -inf; head mapping h = hq / G; split s covers keys
+ *   [s*C, (s+1)*C) clipped to [0, L), with one split length C for the whole
+ *   batch (callers take C = 16*ceil(ceil(maxL/16)/S)); an empty split gives
  *   (O_s = 0, LSE_s = -inf); the combine is the max-shifted log-sum-exp merge.
  */
 #include <math.h>
@@ -102,7 +103,7 @@ typedef struct {
     double *lse;                  /* [nrows]                               */
     /* split model (optional) */
     int num_splits;
-    int granule;
+    int split_keys;    /* keys per split, C                                */
     int block;
     double *o_part;               /* [S][nrows][d]                         */
     double *lse_part;             /* [S][nrows]                            */
@@ -188,11 +189,9 @@ static void attend_online(const problem_t *P, int r, int j0, int j1, double *o, 
     *lse = m + log(l);
 }
 
-/* Split s of a row with L keys: units of `granule` keys, T = ceil(units/S). */
-static void split_range(int L, int S, int granule, int s, int *j0, int *j1) {
-    int units = (L + granule - 1) / granule;
-    int T = (units + S - 1) / S;
-    long a = (long)s * T * granule, b = (long)(s + 1) * T * granule;
+/* Split s of a row with L keys covers [s*C, (s+1)*C) clipped to [0, L). */
+static void split_range(int L, int C, int s, int *j0, int *j1) {
+    long a = (long)s * C, b = (long)(s + 1) * C;
     if (a > L) a = L;
     if (b > L) b = L;
     *j0 = (int)a;
@@ -215,7 +214,7 @@ static void *run_rows(void *arg) {
             int s;
             for (s = 0; s < P->num_splits; ++s) {
                 int j0, j1;
-                split_range(P->len[r], P->num_splits, P->granule, s, &j0, &j1);
+                split_range(P->len[r], P->split_keys, s, &j0, &j1);
                 attend_online(P, r, j0, j1, P->o_part + ((size_t)s * P->nrows + r) * P->d,
                               P->lse_part + (size_t)s * P->nrows + r);
             }
@@ -406,12 +405,15 @@ int oracle_dense_attention(int hq, int hkv, int qlen, int kvlen, int d, int dtyp
 int oracle_paged_split_partials(int B, int qlen, int hq, int hkv, int d, int page_size,
                                 int max_pages, int dtype, const uint16_t *q, const uint16_t *kc,
                                 const uint16_t *vc, const int32_t *block_table,
-                                const int32_t *seqlens, double scale, int num_splits, int granule,
+                                const int32_t *seqlens, double scale, int num_splits, int split_keys,
                                 int block, int nthreads, double *o_part, double *lse_part) {
     tables_t T;
     problem_t P;
     int nrows = B * qlen * hq;
-    if (check_common(hq, hkv, d) || page_size <= 0 || num_splits < 1 || granule < 1) return -1;
+    int b;
+    if (check_common(hq, hkv, d) || page_size <= 0 || num_splits < 1 || split_keys < 1) return -1;
+    for (b = 0; b < B; ++b) /* the splits must cover every key */
+        if ((long)num_splits * split_keys < seqlens[b]) return -1;
     memset(&T, 0, sizeof(T));
     if (build_paged(&T, B, qlen, hq, hkv, d, page_size, max_pages, q, kc, vc, block_table, seqlens)) {
         free_tables(&T, nrows);
@@ -422,7 +424,7 @@ int oracle_paged_split_partials(int B, int qlen, int hq, int hkv, int d, int pag
     P.qrow = T.qrow; P.len = T.len;
     P.krow = (const uint16_t *const *const *)T.krow;
     P.vrow = (const uint16_t *const *const *)T.vrow;
-    P.num_splits = num_splits; P.granule = granule; P.block = block;
+    P.num_splits = num_splits; P.split_keys = split_keys; P.block = block;
     P.o_part = o_part; P.lse_part = lse_part;
     run_problem(&P, nthreads);
     free_tables(&T, nrows);
@@ -432,11 +434,12 @@ int oracle_paged_split_partials(int B, int qlen, int hq, int hkv, int d, int pag
 /* Split partials, dense layout.  Rows n = hq*qlen+i. */
 int oracle_dense_split_partials(int hq, int hkv, int qlen, int kvlen, int d, int dtype,
                                 const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                double scale, int num_splits, int granule, int block, int nthreads,
-                                double *o_part, double *lse_part) {
+                                double scale, int num_splits, int split_keys, int block,
+                                int nthreads, double *o_part, double *lse_part) {
     tables_t T;
     problem_t P;
-    if (check_common(hq, hkv, d) || kvlen < 0 || num_splits < 1 || granule < 1) return -1;
+    if (check_common(hq, hkv, d) || kvlen < 0 || num_splits < 1 || split_keys < 1) return -1;
+    if ((long)num_splits * split_keys < kvlen) return -1; /* the splits must cover every key */
     memset(&T, 0, sizeof(T));
     build_dense(&T, hq, hkv, qlen, kvlen, d, q, k, v);
     memset(&P, 0, sizeof(P));
@@ -444,7 +447,7 @@ int oracle_dense_split_partials(int hq, int hkv, int qlen, int kvlen, int d, int
     P.qrow = T.qrow; P.len = T.len;
     P.krow = (const uint16_t *const *const *)T.krow;
     P.vrow = (const uint16_t *const *const *)T.vrow;
-    P.num_splits = num_splits; P.granule = granule; P.block = block;
+    P.num_splits = num_splits; P.split_keys = split_keys; P.block = block;
     P.o_part = o_part; P.lse_part = lse_part;
     run_problem(&P, nthreads);
     free_tables(&T, hq * qlen);

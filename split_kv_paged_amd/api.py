@@ -196,3 +196,51 @@ def check_paged_inputs(shape_args, block_table_host, cache_seqlens_host, num_pag
                                              sl.ctypes.data_as(ctypes.c_void_p),
                                              int(num_pages), ctypes.byref(bad))
     return _L.STATUS[code], bad.value
+
+
+class PreparedDecode:
+    """A decode call with its arguments marshalled once, for tight loops.
+
+    Holds the shape struct and pointers of one set of tensors; each call
+    re-enters attn_decode_fwd (which plans and validates again on the host)
+    with only the KV pointers optionally swapped.  The tensors must stay
+    alive and keep their shapes for the object's lifetime.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0,
+                 pack_gqa=-1, softmax_scale=None, max_seqlen_k=None, out=None, lse=None,
+                 workspace=None, stream=None):
+        _need(q.dtype in _DT and k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
+              "q, k_cache, v_cache must share fp16 or bf16")
+        dev = _check_dev(q, k_cache, v_cache, block_table, cache_seqlens, out, lse, workspace)
+        self.shape = decode_shape(q, k_cache, block_table, max_seqlen_k)
+        self.lib = _L.load()
+        plan = _L.Plan()
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        _L.check("attn_decode_plan", self.lib.attn_decode_plan(
+            ctypes.byref(self.shape), num_splits, pack_gqa, cus, ctypes.byref(plan)))
+        self.plan = plan
+        self.out = out if out is not None else torch.empty_like(q)
+        self.lse = lse if lse is not None else torch.empty(
+            (q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
+        if workspace is None and plan.workspace_bytes > 0:
+            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self._keep = (q, k_cache, v_cache, block_table, cache_seqlens)
+        self.args = [ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                     _ptr(block_table), _ptr(cache_seqlens), int(num_splits), int(pack_gqa),
+                     float(softmax_scale) if softmax_scale else 0.0, _ptr(self.out),
+                     _ptr(self.lse), _ptr(workspace),
+                     workspace.numel() if workspace is not None else 0, _stream(dev, stream)]
+        self.fn = self.lib.attn_decode_fwd
+
+    def __call__(self, k_cache=None, v_cache=None):
+        a = self.args
+        if k_cache is not None:
+            a = list(a)
+            a[2] = ctypes.c_void_p(k_cache.data_ptr())
+            a[3] = ctypes.c_void_p(v_cache.data_ptr())
+        code = self.fn(*a)
+        if code:
+            _L.check("attn_decode_fwd", code)
+        return self.out, self.lse

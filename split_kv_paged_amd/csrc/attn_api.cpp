@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -20,6 +21,12 @@ constexpr int kMaxSplitsRule = 128; // candidate split counts tried by the rule
 constexpr int kMaxSplits = 1024;    // largest split count a caller may ask for
 constexpr int kDefaultCus = 256;    // one MI355X
 constexpr int kMaxRowsPerBlock = 8;
+constexpr int kMfmaRows = 16;
+constexpr int kMfmaKernelId = 10000;
+#ifndef SKV_USE_VALU
+#define SKV_USE_VALU 0
+#endif
+constexpr bool kUseMfma = !SKV_USE_VALU;
 constexpr int kMaxDevices = 64;
 
 thread_local attn_plan g_last_plan;
@@ -93,14 +100,21 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   if (splits > 1) pack = true;  // same article, section "常见坑点"
 
   const int64_t rows_per_unit = pack ? int64_t(q_len) * group : q_len;
-  const int rpb = rows_per_block_for(int(rows_per_unit > kMaxRowsPerBlock ? kMaxRowsPerBlock
-                                                                           : rows_per_unit));
+  // matrix-core kernel: 16 packed rows per workgroup; VALU kernel: 1..8
+  const int rpb = kUseMfma ? kMfmaRows
+                           : rows_per_block_for(int(rows_per_unit > kMaxRowsPerBlock
+                                                        ? kMaxRowsPerBlock
+                                                        : rows_per_unit));
   const int64_t row_blocks = ceil_div(rows_per_unit, rpb);
   const int64_t unit_heads = pack ? hkv : hq;
   const int64_t units = batch * unit_heads * row_blocks;
   const int64_t grid = units * splits;
   if (grid > INT32_MAX || rows_per_unit > INT32_MAX) return ATTN_ERR_SHAPE;
   const int64_t nrows = batch * q_len * int64_t(hq);
+  // one split length for the batch: whole 16-key granules, S of them cover max_seqlen_k
+  const int64_t split_keys =
+      int64_t(kGranule) * std::max<int64_t>(1, ceil_div(ceil_div(max_seqlen_k, kGranule), splits));
+  if (split_keys > INT32_MAX) return ATTN_ERR_SHAPE;
   int64_t ws = 0;
   if (splits > 1)
     ws = round_up(int64_t(splits) * nrows * head_dim * 4, 256) + round_up(int64_t(splits) * nrows * 4, 256);
@@ -116,7 +130,8 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   out->split_granule = kGranule;
   out->num_cus = num_cus;
   out->combine = splits > 1 ? 1 : 0;
-  out->kernel = skv::split_variant_id({0, head_dim, rpb, !dense});
+  out->kernel = (kUseMfma ? kMfmaKernelId : 0) + skv::split_variant_id({0, head_dim, rpb, !dense});
+  out->split_keys = int(split_keys);
   out->workspace_bytes = ws;
   return ATTN_OK;
 }
@@ -176,6 +191,7 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
                 void* out, float* lse, void* ws, hipStream_t stream) {
   const int S = plan.num_splits;
   prm.num_splits = S;
+  prm.split_keys = plan.split_keys;
   prm.rows = plan.rows_per_unit;
   prm.row_blocks = plan.row_blocks;
   prm.heads_per_unit = plan.pack_gqa ? prm.group : 1;
@@ -187,9 +203,15 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
     prm.o_part = static_cast<float*>(ws);
     prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
   }
-  skv::SplitVariant var{dtype, head_dim, plan.rows_per_block, paged};
-  if (!skv::split_variant_supported(var)) return ATTN_ERR_UNSUPPORTED;
-  if (skv::launch_split(var, prm, plan.grid, stream) != hipSuccess) return ATTN_ERR_HIP;
+  hipError_t err;
+  if (plan.kernel >= kMfmaKernelId) {
+    err = skv::launch_split_mfma(dtype, head_dim, paged, prm, plan.grid, stream);
+  } else {
+    skv::SplitVariant var{dtype, head_dim, plan.rows_per_block, paged};
+    if (!skv::split_variant_supported(var)) return ATTN_ERR_UNSUPPORTED;
+    err = skv::launch_split(var, prm, plan.grid, stream);
+  }
+  if (err != hipSuccess) return ATTN_ERR_HIP;
   if (S > 1) {
     skv::CombineParams c{};
     c.o_part = prm.o_part;

@@ -27,6 +27,7 @@ struct SplitParams {
   int batch, q_len, hq, hkv, group;  // group = Hq / Hkv
   int page_size, max_pages, kv_len;
   int num_splits;
+  int split_keys;      // keys per split (multiple of 16); split s = [s*C, (s+1)*C)
   int rows;            // valid rows per unit (q_len * heads_per_unit)
   int row_blocks;      // ceil(rows / R)
   int heads_per_unit;  // group (packed) or 1
@@ -57,6 +58,9 @@ struct SplitVariant {
 };
 
 hipError_t launch_split(const SplitVariant& v, const SplitParams& p, int grid, hipStream_t s);
+// matrix-core variant: 16 packed rows per workgroup, head_dim 64 or 128
+hipError_t launch_split_mfma(int dtype, int head_dim, bool paged, const SplitParams& p, int grid,
+                             hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t s);
 bool split_variant_supported(const SplitVariant& v);
 int split_variant_id(const SplitVariant& v);

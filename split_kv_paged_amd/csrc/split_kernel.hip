@@ -7,9 +7,11 @@
 //     "两个开关在 kernel 层面各做了什么"): the G query heads of one KV head
 //     (times q_len) are the rows of one unit, so each K/V byte is read once
 //     for all of them;
-//   * split s covers keys [s*T*16, (s+1)*T*16) clipped to L, with
-//     T = ceil(ceil(L/16)/S); a split emits its partial output and LSE, and
-//     a separate combine pass merges them (same article and section);
+//   * split s covers keys [s*C, (s+1)*C) clipped to L, with one split length
+//     C = 16*ceil(ceil(max_seqlen_k/16)/S) for the whole batch, so a split's
+//     first key does not depend on the sequence's length; a split emits its
+//     partial output and LSE, and a separate combine pass merges them (same
+//     article and section);
 //   * online softmax with a running max m, running sum l and an fp32
 //     accumulator rescaled by 2^(m_old - m_new) (ai6s.net FlashAttention
 //     article, section "FlashAttention 的数学细节"), in base 2 with
@@ -35,6 +37,8 @@
 // softmax: numerator and denominator share the reference).  At the end the
 // groups of a wave are merged with shuffles, and the waves of the workgroup
 // through LDS, by the log-sum-exp rules.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace skv {
@@ -65,6 +69,12 @@ struct Elem<0> {  // IEEE binary16
   static __device__ __forceinline__ uint16_t round(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
   }
+  // (a, b) rounded to nearest-even, a in the low half
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, half2_t));
+  }
+  static constexpr uint32_t kOnePair = 0x3C003C00u;  // (1.0, 1.0)
 };
 
 template <>
@@ -82,6 +92,11 @@ struct Elem<1> {  // bfloat16
   static __device__ __forceinline__ uint16_t round(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, bf162_t));
+  }
+  static constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0)
 };
 
 template <int CTRL>
@@ -101,10 +116,28 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float shfl_xor(float x, int mask) {
-  const int lane = threadIdx.x & 63;
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
+// All-reduce over the key groups of a wave: lanes that differ in the bits
+// above log2(LPT) (same chunk lane j).  Inside a 16-lane row the groups are
+// combined by DPP row rotations; across rows by the gfx950 permlane16/32
+// swaps.  Everything stays in VGPRs (no LDS traffic).
+template <int LPT, bool MAX>
+__device__ __forceinline__ float groups_reduce(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (LPT <= 4) x = op(x, dpp<0x124>(x));  // row_ror:4
+  if constexpr (LPT <= 8) x = op(x, dpp<0x128>(x));  // row_ror:8
+  {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                      __builtin_bit_cast(unsigned, x), false,
+                                                      false);
+    x = op(__builtin_bit_cast(float, (unsigned)s16[0]), __builtin_bit_cast(float, (unsigned)s16[1]));
+  }
+  {
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                      __builtin_bit_cast(unsigned, x), false,
+                                                      false);
+    x = op(__builtin_bit_cast(float, (unsigned)s32[0]), __builtin_bit_cast(float, (unsigned)s32[1]));
+  }
+  return x;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -119,13 +152,15 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
 }
 
-template <int DT, int D, int R, int LPT, int NW, bool PAGED>
+template <int DT, int D, int R, int LPT, int NW, int NBUF, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void split_kernel(const SplitParams p) {
   using E = Elem<DT>;
   constexpr int TPS = 64 / LPT;     // keys per step
   constexpr int NS = kTile / TPS;   // steps per tile
   constexpr int CPL = D / (8 * LPT);  // 16-byte chunks per lane per key
   static_assert(NS >= 1 && CPL >= 1 && TPS * NS == kTile && CPL * 8 * LPT == D, "tiling");
+  static_assert(NBUF >= 2, "at least one tile in flight while one is computed");
+  static_assert(NS % 2 == 0, "PV pairs the keys of two steps");
 
   struct Buf {
     uint4 k[NS][CPL];
@@ -148,12 +183,24 @@ __global__ __launch_bounds__(NW * 64) void split_kernel(const SplitParams p) {
   const int hq0 = uh * p.heads_per_unit;
   const int h = hq0 / p.group;
 
+  // The split's first key is known without the sequence length, so the
+  // page ids of this wave's first tiles, the query rows and the length are
+  // all fetched in one round trip.  Lane i of a wave holds the page id of
+  // the wave's tile cb + i (tiles are dealt to waves round-robin), for one
+  // chunk of 64 tiles at a time; the loop reads it with v_readlane.
+  const int t0 = split * p.split_keys;
+  auto load_pages = [&](int cb) -> int {
+    if constexpr (PAGED) {
+      const int tt = t0 + (wave + (cb + lane) * NW) * kTile;
+      return p.block_table[(long)b * p.max_pages + min(tt / p.page_size, p.max_pages - 1)];
+    } else {
+      return 0;
+    }
+  };
+  int pages = load_pages(0);
   const int L = PAGED ? p.seqlens[b] : p.kv_len;
-  const int units = (L + kTile - 1) / kTile;
-  const int per = (units + p.num_splits - 1) / p.num_splits;
-  const int t0 = min(split * per * kTile, L);
-  const int t1 = min((split + 1) * per * kTile, L);
-  const int n_tiles = (t1 - t0 + kTile - 1) / kTile;
+  const int t1 = min(t0 + p.split_keys, L);
+  const int n_tiles = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
   // ---- query rows (raw 16-bit pairs, in the lane's chunk order) ----------
@@ -193,20 +240,6 @@ __global__ __launch_bounds__(NW * 64) void split_kernel(const SplitParams p) {
   const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.k);
   const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(p.v);
 
-  // Physical page of a tile: a wave-uniform scalar load through the constant
-  // address space, so it is tracked by lgkmcnt and never waits on the
-  // vector loads in flight.
-  typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
-  const const_i32_ptr bt = PAGED ? (const_i32_ptr)(p.block_table + (long)b * p.max_pages) : nullptr;
-  auto page_of = [&](int idx) -> int {
-    if constexpr (PAGED) {
-      const int tt = t0 + (wave + idx * NW) * kTile;
-      return bt[tt / p.page_size];
-    } else {
-      return 0;
-    }
-  };
-
   // element offset of key row 0 of tile idx, KV head h
   auto tile_row0 = [&](int idx, int page) -> long {
     const int tt = t0 + (wave + idx * NW) * kTile;
@@ -229,6 +262,8 @@ __global__ __launch_bounds__(NW * 64) void split_kernel(const SplitParams p) {
   // belonging to the next split, or past the end of a dense tensor) read as
   // zero and never fault.
   auto issue = [&](Buf& bf, int idx, int page) {
+    // the page id is wave-uniform; say so, so the descriptors stay in SGPRs
+    page = __builtin_amdgcn_readfirstlane(page);
     const int tt = t0 + (wave + idx * NW) * kTile;
     const long row0 = tile_row0(idx, page);
     const uint32_t bytes = uint32_t(min(kTile, t1 - tt) * row_stride * 2);
@@ -243,35 +278,43 @@ __global__ __launch_bounds__(NW * 64) void split_kernel(const SplitParams p) {
       }
   };
 
-  auto process = [&](const Buf& bf, int idx) {
-    const int tt = t0 + (wave + idx * NW) * kTile;
-    const bool full = tt + kTile <= t1;
-    float sc[NS][R];
+  // One tile: scores, lazy reference update, probabilities rounded to the
+  // 16-bit type in pairs of keys, and PV as v_dot2 over those key pairs (the
+  // running sum l takes the same rounded values, so numerator and
+  // denominator use identical weights).  FULL tiles skip the key mask.
+  const float c = p.scale_log2;
+  auto process_tile = [&](const Buf& bf, int tt, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    float dr[NS][R];  // raw q.k per key step and row
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const bool valid = full || (tt + st * TPS + sub < t1);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          d = E::dot2(qv[r][c][0], bf.k[st][c].x, d);
-          d = E::dot2(qv[r][c][1], bf.k[st][c].y, d);
-          d = E::dot2(qv[r][c][2], bf.k[st][c].z, d);
-          d = E::dot2(qv[r][c][3], bf.k[st][c].w, d);
+        for (int cc = 0; cc < CPL; ++cc) {
+          d = E::dot2(qv[r][cc][0], bf.k[st][cc].x, d);
+          d = E::dot2(qv[r][cc][1], bf.k[st][cc].y, d);
+          d = E::dot2(qv[r][cc][2], bf.k[st][cc].z, d);
+          d = E::dot2(qv[r][cc][3], bf.k[st][cc].w, d);
         }
-        d = group_sum<LPT>(d);
-        sc[st][r] = valid ? d * p.scale_log2 : -INFINITY;
+        dr[st][r] = group_sum<LPT>(d);
+      }
+      if constexpr (!FULL) {
+        const bool valid = tt + st * TPS + sub < t1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) dr[st][r] = valid ? dr[st][r] : -INFINITY;
       }
     }
-    // lazy reference update
+    // lazy reference update (scale > 0, so the max commutes with it)
     bool need = false;
     float mnew[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float mt = sc[0][r];
+      float mt = dr[0][r];
 #pragma unroll
-      for (int st = 1; st < NS; ++st) mt = fmaxf(mt, sc[st][r]);
+      for (int st = 1; st < NS; ++st) mt = fmaxf(mt, dr[st][r]);
+      mt *= c;
       mnew[r] = (mt > m[r] + kRescaleHeadroom) ? mt : m[r];
       need |= mnew[r] != m[r];
     }
@@ -285,74 +328,86 @@ __global__ __launch_bounds__(NW * 64) void split_kernel(const SplitParams p) {
         for (int e = 0; e < CPL * 8; ++e) acc[r][e] *= alpha;
       }
     }
-    float pr[NS][R];
+    // probabilities of key steps (2sp, 2sp+1), packed
+    uint32_t pp[NS / 2][R];
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
+    for (int sp = 0; sp < NS / 2; ++sp)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        pr[st][r] = (sc[st][r] == -INFINITY) ? 0.f : fast_exp2(sc[st][r] - m[r]);
-        l[r] += pr[st][r];
+        float p0 = fast_exp2(fmaf(dr[2 * sp][r], c, -m[r]));
+        float p1 = fast_exp2(fmaf(dr[2 * sp + 1][r], c, -m[r]));
+        if constexpr (!FULL) {  // masked keys; m may still be -inf here
+          p0 = (dr[2 * sp][r] == -INFINITY) ? 0.f : p0;
+          p1 = (dr[2 * sp + 1][r] == -INFINITY) ? 0.f : p1;
+        }
+        pp[sp][r] = E::pack(p0, p1);
+        l[r] = E::dot2(pp[sp][r], E::kOnePair, l[r]);
       }
+    // PV: pair the value rows of keys 2sp and 2sp+1 element by element
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
+    for (int sp = 0; sp < NS / 2; ++sp)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        // rows past the split were read as zero, so p = 0 meets v = 0 there
-        const uint32_t w4[4] = {bf.v[st][c].x, bf.v[st][c].y, bf.v[st][c].z, bf.v[st][c].w};
+      for (int cc = 0; cc < CPL; ++cc) {
+        const uint32_t a4[4] = {bf.v[2 * sp][cc].x, bf.v[2 * sp][cc].y, bf.v[2 * sp][cc].z,
+                                bf.v[2 * sp][cc].w};
+        const uint32_t b4[4] = {bf.v[2 * sp + 1][cc].x, bf.v[2 * sp + 1][cc].y,
+                                bf.v[2 * sp + 1][cc].z, bf.v[2 * sp + 1][cc].w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float v0 = E::lo(w4[w]);
-          const float v1 = E::hi(w4[w]);
+          const uint32_t lo = __builtin_amdgcn_perm(b4[w], a4[w], 0x05040100u);  // elem 2w
+          const uint32_t hi = __builtin_amdgcn_perm(b4[w], a4[w], 0x07060302u);  // elem 2w+1
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            acc[r][c * 8 + 2 * w] = fmaf(pr[st][r], v0, acc[r][c * 8 + 2 * w]);
-            acc[r][c * 8 + 2 * w + 1] = fmaf(pr[st][r], v1, acc[r][c * 8 + 2 * w + 1]);
+            acc[r][cc * 8 + 2 * w] = E::dot2(lo, pp[sp][r], acc[r][cc * 8 + 2 * w]);
+            acc[r][cc * 8 + 2 * w + 1] = E::dot2(hi, pp[sp][r], acc[r][cc * 8 + 2 * w + 1]);
           }
         }
       }
-    }
+  };
+  auto process = [&](const Buf& bf, int idx) {
+    const int tt = t0 + (wave + idx * NW) * kTile;
+    if (tt + kTile <= t1)
+      process_tile(bf, tt, std::true_type{});
+    else
+      process_tile(bf, tt, std::false_type{});
   };
 
-  // ---- main loop: double-buffered tiles ----------------------------------
-  // Loads of tile n+1 are issued before tile n is computed; the page id is
-  // fetched one tile further ahead.  Indices past the last tile are clamped
-  // (a redundant, cached re-read) so every load is unconditional.
-  if (my_tiles > 0) {
-    Buf A, B;
-    const int last = my_tiles - 1;
-    int pg = page_of(0);
-    issue(A, 0, pg);
-    pg = page_of(min(1, last));
-    int idx = 0;
-    while (true) {
-      issue(B, min(idx + 1, last), pg);
-      pg = page_of(min(idx + 2, last));
-      process(A, idx);
-      if (++idx >= my_tiles) break;
-      issue(A, min(idx + 1, last), pg);
-      pg = page_of(min(idx + 2, last));
-      process(B, idx);
-      if (++idx >= my_tiles) break;
+  // ---- main loop: NBUF tiles in a register ring ----------------------------
+  // The loads of tiles n+1 .. n+NBUF-1 are in flight while tile n is
+  // computed.  Indices past the chunk's last tile are clamped (a redundant,
+  // cached re-read), so every load is unconditional, and nothing but the
+  // tile index is carried from one iteration to the next.
+  for (int cb = 0; cb < my_tiles; cb += 64) {
+    if (cb > 0) pages = load_pages(cb);
+    const int n = min(64, my_tiles - cb);
+    const int last = n - 1;
+    auto page_at = [&](int i) { return __builtin_amdgcn_readlane(pages, i); };
+    Buf ring[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k) issue(ring[k], cb + min(k, last), page_at(min(k, last)));
+    int i = 0;
+    bool more = true;
+    while (more) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        if (more) {
+          const int nx = min(i + NBUF - 1, last);
+          issue(ring[(k + NBUF - 1) % NBUF], cb + nx, page_at(nx));
+          process(ring[k], cb + i);
+          more = ++i < n;
+        }
+      }
     }
   }
 
   // ---- merge the key groups of this wave (lanes differing in `sub`) ------
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float M = m[r];
-#pragma unroll
-    for (int x = LPT; x < 64; x <<= 1) M = fmaxf(M, shfl_xor(M, x));
+    const float M = groups_reduce<LPT, true>(m[r]);
     const float f = (m[r] == -INFINITY) ? 0.f : fast_exp2(m[r] - M);
-    l[r] *= f;
+    l[r] = groups_reduce<LPT, false>(l[r] * f);
 #pragma unroll
-    for (int x = LPT; x < 64; x <<= 1) l[r] += shfl_xor(l[r], x);
-#pragma unroll
-    for (int e = 0; e < CPL * 8; ++e) {
-      float a = acc[r][e] * f;
-#pragma unroll
-      for (int x = LPT; x < 64; x <<= 1) a += shfl_xor(a, x);
-      acc[r][e] = a;
-    }
+    for (int e = 0; e < CPL * 8; ++e) acc[r][e] = groups_reduce<LPT, false>(acc[r][e] * f);
     m[r] = M;
   }
 
@@ -409,19 +464,32 @@ __global__ __launch_bounds__(NW * 64) void split_kernel(const SplitParams p) {
   }
 }
 
-// kernel choice per (head_dim, rows per block): lanes per key and waves
+// kernel choice per (head_dim, rows per block): lanes per key, waves per
+// workgroup and tiles in the register ring
+#ifndef SKV_NW
+#define SKV_NW 8
+#endif
+#ifndef SKV_NBUF
+#define SKV_NBUF 2
+#endif
+#ifndef SKV_LPT_R4
+#define SKV_LPT_R4 16  // lanes per key (x D/128) when a block carries <= 4 rows
+#endif
 template <int D, int R>
 struct Cfg {
-  static constexpr int LPT = (R <= 4) ? D / 16 : D / 8;
-  static constexpr int NW = 8;
+  static constexpr int LPT_R4 = SKV_LPT_R4 * D / 128 < 8 ? 8 : SKV_LPT_R4 * D / 128;
+  static constexpr int LPT = (R <= 4) ? LPT_R4 : D / 8;
+  static constexpr int NW = SKV_NW;
+  static constexpr int NBUF = SKV_NBUF;
 };
 
 template <int DT, int D, int R, bool PAGED>
 hipError_t launch_one(const SplitParams& p, int grid, hipStream_t s) {
   constexpr int LPT = Cfg<D, R>::LPT;
   constexpr int NW = Cfg<D, R>::NW;
-  hipLaunchKernelGGL((split_kernel<DT, D, R, LPT, NW, PAGED>), dim3(grid), dim3(NW * 64), 0, s,
-                     p);
+  constexpr int NBUF = Cfg<D, R>::NBUF;
+  hipLaunchKernelGGL((split_kernel<DT, D, R, LPT, NW, NBUF, PAGED>), dim3(grid), dim3(NW * 64), 0,
+                     s, p);
   return hipGetLastError();
 }
 

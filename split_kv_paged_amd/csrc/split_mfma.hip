@@ -1,0 +1,398 @@
+// split_mfma.hip -- split-KV decode / small-query attention on gfx950 matrix cores.
+//
+// Same work decomposition, split ranges, online softmax and epilogue as the
+// VALU kernel (split_kernel.hip); only the two contractions move to MFMA:
+//
+//   S^T (16 keys x 16 rows) = K (16 x D) . Q^T (D x 16)
+//       v_mfma_f32_16x16x32_{bf16,f16}, D/32 instructions per 16-key tile.
+//       With K as the A operand, lane l holds the scores of query row l%16
+//       for keys 4*(l/16)..+3: one row per lane, so the softmax needs no
+//       per-key lane reductions, and the probabilities, rounded to the
+//       16-bit type, are already the A operand of the next product.
+//   O (16 rows x D) += P (16 x 16 keys) . V (16 keys x D)
+//       v_mfma_f32_16x16x16_{bf16,f16}, D/16 instructions per tile, plus one
+//       more with an all-ones B operand whose output column is the running
+//       sum of the rounded probabilities: O is divided by exactly the
+//       weights it was built from.  The LSE uses a float32 running sum of
+//       the unrounded probabilities.
+//       The V tile is staged in LDS by each wave and read back with
+//       ds_read_b64_tr_b16, which delivers the key-major B operand.
+//
+// Packed query rows beyond the unit's real rows are zero; their lanes do the
+// same (SIMD) work and are never written.  A unit carries at most 16 rows.
+//
+// Sources: attention definition (SmallQ FlashAttention README, section 接口);
+// online softmax with max offset (ai6s.net FlashAttention article, section
+// "FlashAttention 的数学细节"); GQA packing and split partials with their
+// logsumexp (lpnh.cn "pack_gqa 与 num_splits" article, section
+// "两个开关在 kernel 层面各做了什么"); fp32 accumulation (SmallQ README,
+// section 精度策略).
+#include <type_traits>
+
+#include "internal.h"
+
+namespace skv {
+namespace {
+
+constexpr int kTile = 16;
+constexpr float kHeadroom = 8.0f;  // log2 units before the reference moves
+constexpr float kLn2 = 0.693147180559945309417f;
+
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct Mf;
+
+template <>
+struct Mf<1> {  // bfloat16
+  static __device__ __forceinline__ f4_t qk(uint4 a, uint4 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a),
+                                                   __builtin_bit_cast(bf8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f4_t pv(uint2 a, uint2 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a),
+                                                     __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, bf2_t));
+  }
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static constexpr uint32_t kOnePair = 0x3F803F80u;
+};
+
+template <>
+struct Mf<0> {  // IEEE binary16
+  static __device__ __forceinline__ f4_t qk(uint4 a, uint4 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
+                                                  __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f4_t pv(uint2 a, uint2 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a),
+                                                 __builtin_bit_cast(h4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, h2_t));
+  }
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static constexpr uint32_t kOnePair = 0x3C003C00u;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48)
+template <bool MAX>
+__device__ __forceinline__ float across_rows(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+  x = op(__builtin_bit_cast(float, (unsigned)s16[0]), __builtin_bit_cast(float, (unsigned)s16[1]));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+  return op(__builtin_bit_cast(float, (unsigned)s32[0]), __builtin_bit_cast(float, (unsigned)s32[1]));
+}
+
+__device__ __forceinline__ float from_lane(float x, int src_lane) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, x)));
+}
+
+template <int DT, int D, int NW, int NBUF, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
+  using M = Mf<DT>;
+  constexpr int KB = D / 32;        // 16x16x32 products per tile (QK)
+  constexpr int DB = D / 16;        // 16x16x16 products per tile (PV)
+  constexpr int ROWB = D * 2 + 32;  // LDS bytes per staged V key row (+32 against bank clashes)
+  static_assert(D % 32 == 0, "head_dim");
+
+  struct Buf {
+    uint4 k[KB];
+    uint4 v[KB];
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;  // S^T: query row; O: column within a 16-wide d block
+  const int g = lane >> 4;    // S^T: key group (keys 4g..4g+3); O: rows 4g..4g+3
+
+  int bid = blockIdx.x;
+  const int split = bid % p.num_splits;
+  bid /= p.num_splits;
+  const int rb = bid % p.row_blocks;
+  bid /= p.row_blocks;
+  const int uh = bid % p.unit_heads;
+  const int b = bid / p.unit_heads;
+  const int hq0 = uh * p.heads_per_unit;
+  const int h = hq0 / p.group;
+
+  // split range and this wave's tiles (round-robin over the waves)
+  const int t0 = split * p.split_keys;
+  auto load_pages = [&](int cb) -> int {
+    if constexpr (PAGED) {
+      const int tt = t0 + (wave + (cb + lane) * NW) * kTile;
+      return p.block_table[(long)b * p.max_pages + min(tt / p.page_size, p.max_pages - 1)];
+    } else {
+      return 0;
+    }
+  };
+  int pages = load_pages(0);
+  const int L = PAGED ? p.seqlens[b] : p.kv_len;
+  const int t1 = min(t0 + p.split_keys, L);
+  const int n_tiles = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
+
+  // ---- Q^T as the B operand: lane l holds row l%16, chunks g*KB + kb -----
+  const int rowq = rb * 16 + n16;  // packed row of this lane in S^T
+  uint4 qb[KB];
+  {
+    bool real = rowq < p.rows;
+    long n = 0;
+    if (real) {
+      const int i = rowq / p.heads_per_unit;
+      const int hq = hq0 + rowq % p.heads_per_unit;
+      n = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
+    }
+    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * D);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qb[kb] = real ? qp[g * KB + kb] : make_uint4(0, 0, 0, 0);
+  }
+
+  f4_t acc[DB + 1];  // O blocks; acc[DB] is the all-ones block: column sums = l
+#pragma unroll
+  for (int db = 0; db <= DB; ++db) acc[db] = (f4_t){0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // reference max of row n16 (S^T layout), log2 units
+  float l32 = 0.f;      // float32 sum of this lane's probabilities (row n16)
+
+  const long row_stride = PAGED ? (long)p.hkv * D : (long)D;
+  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.k);
+  const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(p.v);
+  const int voff = int((n16 * row_stride + g * KB * 8) * 2);  // key n16, bytes [16*KB*g, +16*KB)
+
+  // V staging (NW x 16 padded key rows) during the loop; the same bytes
+  // hold the waves' partial outputs (NW x 16 rows x D floats) for the merge.
+  constexpr int kStage = NW * kTile * ROWB;
+  constexpr int kMerge = NW * 16 * D * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kStage > kMerge ? kStage : kMerge];
+  uint8_t* const my_v = s_buf + wave * kTile * ROWB;
+  typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
+  const uint32_t v_wr = uint32_t(n16 * ROWB + g * KB * 16);  // where this lane's V bytes go
+  // transposed read of d block db: lane 16g + 4i + q reads key 4g+i, d 16db + 4q .. +3
+  const uint32_t v_rd = uint32_t((4 * g + ((lane & 15) >> 2)) * ROWB + (lane & 3) * 8);
+
+  auto tile_row0 = [&](int idx, int page) -> long {
+    const int tt = t0 + (wave + idx * NW) * kTile;
+    if constexpr (PAGED) {
+      return ((long)page * p.page_size + tt % p.page_size) * p.hkv * D + (long)h * D;
+    } else {
+      return ((long)h * p.kv_len + tt) * D;
+    }
+  };
+
+  auto issue = [&](Buf& bf, int idx, int page) {
+    page = __builtin_amdgcn_readfirstlane(page);
+    const int tt = t0 + (wave + idx * NW) * kTile;
+    const long row0 = tile_row0(idx, page);
+    const uint32_t bytes = uint32_t(min(kTile, t1 - tt) * row_stride * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0, bytes);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bf.k[kb] = load16(rk, voff + kb * 16);
+      bf.v[kb] = load16(rv, voff + kb * 16);
+    }
+  };
+
+  const float c = p.scale_log2;
+  auto process_tile = [&](const Buf& bf, int tt, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    // stage V (row-major, padded rows) for the transposed reads
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      *reinterpret_cast<uint4*>(my_v + v_wr + kb * 16) = bf.v[kb];
+    // S^T = K . Q^T
+    f4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s = M::qk(bf.k[kb], qb[kb], s);
+    if constexpr (!FULL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (tt + 4 * g + i < t1) ? s[i] : -INFINITY;
+    }
+    // row max over the tile, lazy reference update
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mt = across_rows<true>(mt) * c;
+    const bool need = mt > m + kHeadroom;
+    if (__any(need)) {
+      const float mnew = need ? mt : m;
+      const float alpha = (mnew == m) ? 1.f : fast_exp2(m - mnew);  // -inf -> 0
+      m = mnew;
+      l32 *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = from_lane(alpha, 4 * g + i);  // O rows 4g+i live in lanes of row 4g+i
+#pragma unroll
+        for (int db = 0; db <= DB; ++db) acc[db][i] *= ai;
+      }
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = fast_exp2(fmaf(s[i], c, -m));
+      if constexpr (!FULL) pr[i] = (s[i] == -INFINITY) ? 0.f : pr[i];
+    }
+    l32 += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const uint2 pa = make_uint2(M::pack(pr[0], pr[1]), M::pack(pr[2], pr[3]));
+    // O += P . V, and the all-ones block for l
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const s4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s4_ptr)(my_v + v_rd + db * 32));
+      acc[db] = M::pv(pa, __builtin_bit_cast(uint2, vt), acc[db]);
+    }
+    acc[DB] = M::pv(pa, make_uint2(M::kOnePair, M::kOnePair), acc[DB]);
+  };
+  auto process = [&](const Buf& bf, int idx) {
+    const int tt = t0 + (wave + idx * NW) * kTile;
+    if (tt + kTile <= t1)
+      process_tile(bf, tt, std::true_type{});
+    else
+      process_tile(bf, tt, std::false_type{});
+  };
+
+  // ---- main loop: NBUF tiles in a register ring (see split_kernel.hip) ---
+  for (int cb = 0; cb < my_tiles; cb += 64) {
+    if (cb > 0) pages = load_pages(cb);
+    const int n = min(64, my_tiles - cb);
+    const int last = n - 1;
+    auto page_at = [&](int i) { return __builtin_amdgcn_readlane(pages, i); };
+    Buf ring[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k) issue(ring[k], cb + min(k, last), page_at(min(k, last)));
+    int i = 0;
+    bool more = true;
+    while (more) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        if (more) {
+          const int nx = min(i + NBUF - 1, last);
+          issue(ring[(k + NBUF - 1) % NBUF], cb + nx, page_at(nx));
+          process(ring[k], cb + i);
+          more = ++i < n;
+        }
+      }
+    }
+  }
+
+  // ---- merge the waves through LDS and write -----------------------------
+  // O layout: lane l holds rows 4g..4g+3, columns 16db + n16; l is acc[DB].
+  // m of row r is held by lanes with n16 == r.
+  __syncthreads();  // the V staging area is reused below
+  constexpr int RMAX = 16;
+  float* s_acc = reinterpret_cast<float*>(s_buf);  // [NW][16][D]
+  __shared__ float s_m[NW][RMAX];
+  __shared__ float s_l[NW][RMAX];    // sums of the rounded probabilities (normalise O)
+  __shared__ float s_l32[NW][RMAX];  // float32 sums (LSE)
+  l32 = across_rows<false>(l32);
+  const int rows_here = min(RMAX, p.rows - rb * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    if (r < rows_here) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) s_acc[((long)wave * RMAX + r) * D + db * 16 + n16] = acc[db][i];
+      if (n16 == 0) s_l[wave][r] = acc[DB][i];
+    }
+  }
+  if (g == 0 && n16 < rows_here) {
+    s_m[wave][n16] = m;
+    s_l32[wave][n16] = l32;
+  }
+  __syncthreads();
+
+  for (int t = threadIdx.x; t < rows_here * D; t += NW * 64) {
+    const int r = t / D;
+    const int d = t % D;
+    const int pr = rb * 16 + r;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][r]);
+    float num = 0.f, den = 0.f, den32 = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = (s_m[w][r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - Mx);
+        num = fmaf(f, s_acc[((long)w * RMAX + r) * D + d], num);
+        den = fmaf(f, s_l[w][r], den);
+        den32 = fmaf(f, s_l32[w][r], den32);
+      }
+    }
+    const float o = (Mx == -INFINITY) ? 0.f : num / den;
+    const float lse = (Mx == -INFINITY) ? -INFINITY : (Mx + log2f(den32)) * kLn2;
+    const int i = pr / p.heads_per_unit;
+    const int hq = hq0 + pr % p.heads_per_unit;
+    const long nrow = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
+    if (p.num_splits == 1) {
+      static_cast<uint16_t*>(p.out)[nrow * D + d] = M::round(o);
+      if (d == 0 && p.lse) p.lse[((long)b * p.hq + hq) * p.q_len + i] = lse;
+    } else {
+      p.o_part[((long)split * p.nrows + nrow) * D + d] = o;
+      if (d == 0) p.lse_part[(long)split * p.nrows + nrow] = lse;
+    }
+  }
+}
+
+#ifndef SKV_MFMA_NW
+#define SKV_MFMA_NW 8
+#endif
+#ifndef SKV_MFMA_NBUF
+#define SKV_MFMA_NBUF 2
+#endif
+
+template <int DT, int D, bool PAGED>
+hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
+  constexpr int NW = SKV_MFMA_NW;
+  constexpr int NBUF = SKV_MFMA_NBUF;
+  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED>), dim3(grid), dim3(NW * 64), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+template <int DT, bool PAGED>
+hipError_t launch_mfma_dt(int head_dim, const SplitParams& p, int grid, hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_mfma_d<DT, 64, PAGED>(p, grid, s);
+    case 128: return launch_mfma_d<DT, 128, PAGED>(p, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_split_mfma(int dtype, int head_dim, bool paged, const SplitParams& p, int grid,
+                             hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (paged)
+    return dtype == 1 ? launch_mfma_dt<1, true>(head_dim, p, grid, s)
+                      : launch_mfma_dt<0, true>(head_dim, p, grid, s);
+  return dtype == 1 ? launch_mfma_dt<1, false>(head_dim, p, grid, s)
+                    : launch_mfma_dt<0, false>(head_dim, p, grid, s);
+}
+
+}  // namespace skv

@@ -39,11 +39,11 @@ class DenseShape(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_splits", "pack_gqa", "rows_per_unit", "rows_per_block", "row_blocks", "units",
-        "grid", "split_granule", "num_cus", "combine", "kernel", "reserved")] + [
+        "grid", "split_granule", "num_cus", "combine", "kernel", "split_keys")] + [
         ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 class AttnError(RuntimeError):

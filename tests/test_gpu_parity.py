@@ -201,9 +201,10 @@ def test_partials_and_combine_separately():
     run_paged(wl, num_splits=S, workspace=ws)
     nrows = 3 * 2 * 8
     o_gpu, l_gpu = api.workspace_partials(ws, plan, nrows, 128)
+    assert plan.split_keys == oracle.split_keys_for(wl.max_seqlen_k, S)
     o_ref, l_ref = oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
-                                               wl.cache_seqlens, "bf16", S, 16, block=16,
-                                               scale=wl.scale)
+                                               wl.cache_seqlens, "bf16", S, plan.split_keys,
+                                               block=16, scale=wl.scale)
     check_f32(o_gpu.cpu().numpy(), o_ref)
     check_lse(l_gpu.cpu().numpy(), l_ref)
     case("combine kernel on the oracle's partials")

@@ -30,8 +30,10 @@ MUTATIONS = [
      "l = l + exp(bmax - m_new) * bsum;"),
     ("combine: unnormalised", "for (e = 0; e < d; ++e) o[e] /= wsum;", ""),
     ("combine: lse without shift", "lse[n] = M + log(wsum);", "lse[n] = log(wsum);"),
-    ("split ranges overlap", "long a = (long)s * T * granule, b = (long)(s + 1) * T * granule;",
-     "long a = (long)s * T * granule, b = (long)(s + 2) * T * granule;"),
+    ("split ranges overlap", "long a = (long)s * C, b = (long)(s + 1) * C;",
+     "long a = (long)s * C, b = (long)(s + 2) * C;"),
+    ("split ranges leave gaps", "long a = (long)s * C, b = (long)(s + 1) * C;",
+     "long a = (long)s * C + 1, b = (long)(s + 1) * C;"),
     ("fp16 subnormal scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     ("bf16 exponent bias", "v = ldexp((double)(128 + f), e - 134);",
      "v = ldexp((double)(128 + f), e - 133);"),

@@ -246,29 +246,50 @@ def test_split_partials_and_combine_equal_direct(block):
     n = 4 * 2 * 8
     ref_o = out.reshape(n, 64)
     ref_l = lse.transpose(0, 2, 1).reshape(n)
-    for S in list(range(1, 17)) + [40]:
+    cases = [(S, oracle.split_keys_for(300, S)) for S in list(range(1, 17)) + [40]]
+    cases += [(43, 7), (3, 100), (1, 300), (2, 1000)]  # other split lengths covering L
+    for S, C in cases:
         o, l = oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
-                                           wl.cache_seqlens, "fp16", S, 16, block=block)
+                                           wl.cache_seqlens, "fp16", S, C, block=block)
         co, cl = oracle.combine(o, l)
         np.testing.assert_allclose(co, ref_o, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(cl, ref_l, rtol=1e-12, atol=1e-12)
 
 
+def test_split_length_rule():
+    assert oracle.split_keys_for(16384, 14) == 16 * 74    # ceil(1024/14) = 74 units
+    assert oracle.split_keys_for(1100, 1) == 1104         # 69 units of 16
+    assert oracle.split_keys_for(1, 4) == 16              # at least one granule
+    assert oracle.split_keys_for(0, 3) == 16
+    with pytest.raises(ValueError):                        # splits must cover every key
+        wl = W.make_paged(72, "fp16", 1, 1, 2, 1, 16, 16, [40])
+        oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                    wl.cache_seqlens, "fp16", 2, 16)
+
+
 def test_split_ranges_cover_keys_once_and_empty_splits_are_neutral():
-    # L = 1 with 4 splits: split 0 holds the key, the other three are empty
+    # L = 1 with 4 splits of 16: split 0 holds the key, the other three are empty
     wl = W.make_paged(81, "bf16", 1, 1, 2, 1, 16, 16, [1])
     o, l = oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
                                        wl.cache_seqlens, "bf16", 4, 16)
     assert np.all(np.isfinite(l[0])) and np.all(np.isneginf(l[1:]))
     assert np.all(o[1:] == 0)
     np.testing.assert_array_equal(o[0, 0], f64(wl.v_cache, "bf16")[wl.block_table[0, 0], 0, 0])
+    # a short sequence only fills the first splits of a long batch's split length
+    wl = W.make_paged(82, "bf16", 2, 1, 2, 1, 16, 16, [20, 100])
+    o, l = oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                       wl.cache_seqlens, "bf16", 4, 32)
+    # rows of sequence 0 are n = 0, 1; keys 0..19 -> split 0 has 20 keys, split 1..3 empty
+    assert np.all(np.isfinite(l[0, :2])) and np.all(np.isneginf(l[1:, :2]))
+    assert np.all(np.isfinite(l[:, 2:]))  # 100 keys reach split 3 (96..99)
 
 
 def test_dense_split_matches_dense_direct():
     wl = W.make_dense(91, "fp16", 4, 2, 3, 1025, 24)
     out, lse = oracle.dense_attention(wl.q, wl.k, wl.v, "fp16")
     for S in (1, 3, 7):
-        o, l = oracle.dense_split_partials(wl.q, wl.k, wl.v, "fp16", S, 64, block=32)
+        o, l = oracle.dense_split_partials(wl.q, wl.k, wl.v, "fp16", S,
+                                           oracle.split_keys_for(1025, S), block=32)
         co, cl = oracle.combine(o, l)
         np.testing.assert_allclose(co, out.reshape(12, 24), rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(cl, lse.reshape(12), rtol=1e-12, atol=1e-12)
