@@ -75,7 +75,7 @@ def main():
                            num_splits=args.num_splits, num_cus=cus)
     out = torch.empty_like(q)
     lse = torch.empty((wl.batch, wl.num_heads_q, wl.q_len), dtype=torch.float32, device=dev)
-    ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    ws = (torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
           if plan.workspace_bytes else None)
     stream = torch.cuda.current_stream(dev)
 

@@ -115,7 +115,9 @@ typedef struct {
     int32_t grid;            /* workgroups of the split kernel = units * S    */
     int32_t split_granule;   /* split lengths are multiples of this many keys  */
     int32_t num_cus;         /* compute units the plan was made for           */
-    int32_t combine;         /* 1 when a combine pass merges S > 1 partials   */
+    int32_t combine;         /* how S > 1 partials are merged: 0 none (S = 1), */
+                             /* 1 a separate combine kernel, 2 inside the      */
+                             /* split kernel by the last split to finish       */
     int32_t kernel;          /* kernel variant id (diagnostic)                */
     int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
@@ -139,9 +141,13 @@ attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int
  *   lse may be NULL (not written).
  *   workspace / workspace_bytes: device scratch of at least
  *     plan.workspace_bytes (0 when S = 1, then workspace may be NULL).
- *     Contents on return: float32 partial outputs [S][rows][head_dim]
- *     followed (at the next 256-byte boundary) by float32 partial LSEs
- *     [S][rows], rows ordered (b, i, hq).
+ *     Layout: float32 partial outputs [S][rows][head_dim], then (at the
+ *     next 256-byte boundary) float32 partial LSEs [S][rows], rows ordered
+ *     (b, i, hq); when plan.combine == 2, then (next 256-byte boundary)
+ *     int32 arrival counters [plan.units].  The counters must be zero
+ *     before the first call that uses the workspace (fill it with zeros
+ *     once); every call leaves them zero again.  Calls that share one
+ *     workspace must not run concurrently.
  * The plan uses the compute-unit count of the current device. */
 attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* block_table,

@@ -108,7 +108,8 @@ def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pa
             lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
                               device=dev)
         if workspace is None and plan.workspace_bytes > 0:
-            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+            # zero-filled: the fused combine's arrival counters start at zero
+            workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         code = lib.attn_decode_fwd(
             ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
@@ -143,7 +144,7 @@ def dense_fwd(q, k, v, num_splits=0, softmax_scale=None, out=None, lse=None, ret
         if lse is None and return_lse:
             lse = torch.empty((hq, qlen), dtype=torch.float32, device=dev)
         if workspace is None and plan.workspace_bytes > 0:
-            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+            workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         code = lib.attn_dense_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), num_splits,
                                   float(softmax_scale) if softmax_scale else 0.0, _ptr(out),
@@ -224,7 +225,7 @@ class PreparedDecode:
         self.lse = lse if lse is not None else torch.empty(
             (q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
         if workspace is None and plan.workspace_bytes > 0:
-            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+            workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         self.workspace = workspace
         self._keep = (q, k_cache, v_cache, block_table, cache_seqlens)
         self.args = [ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),

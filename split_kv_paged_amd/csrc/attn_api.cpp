@@ -116,8 +116,14 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
       int64_t(kGranule) * std::max<int64_t>(1, ceil_div(ceil_div(max_seqlen_k, kGranule), splits));
   if (split_keys > INT32_MAX) return ATTN_ERR_SHAPE;
   int64_t ws = 0;
-  if (splits > 1)
+  if (splits > 1) {
     ws = round_up(int64_t(splits) * nrows * head_dim * 4, 256) + round_up(int64_t(splits) * nrows * 4, 256);
+    if (kUseMfma) {
+      // the fused combine addresses the partials with 32-bit byte offsets
+      if (int64_t(splits) * nrows * head_dim * 4 >= (int64_t(1) << 32)) return ATTN_ERR_UNSUPPORTED;
+      ws += round_up(units * 4, 256);  // arrival counters
+    }
+  }
 
   std::memset(out, 0, sizeof(*out));
   out->num_splits = splits;
@@ -129,7 +135,7 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   out->grid = int(grid);
   out->split_granule = kGranule;
   out->num_cus = num_cus;
-  out->combine = splits > 1 ? 1 : 0;
+  out->combine = splits > 1 ? (kUseMfma ? 2 : 1) : 0;
   out->kernel = (kUseMfma ? kMfmaKernelId : 0) + skv::split_variant_id({0, head_dim, rpb, !dense});
   out->split_keys = int(split_keys);
   out->workspace_bytes = ws;
@@ -198,10 +204,13 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   prm.unit_heads = plan.pack_gqa ? prm.hkv : prm.hq;
   prm.out = out;
   prm.lse = lse;
+  const bool fused = plan.kernel >= kMfmaKernelId;
   if (S > 1) {
     const int64_t o_bytes = round_up(int64_t(S) * prm.nrows * head_dim * 4, 256);
+    const int64_t l_bytes = round_up(int64_t(S) * prm.nrows * 4, 256);
     prm.o_part = static_cast<float*>(ws);
     prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+    if (fused) prm.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + o_bytes + l_bytes);
   }
   hipError_t err;
   if (plan.kernel >= kMfmaKernelId) {
@@ -212,7 +221,7 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
     err = skv::launch_split(var, prm, plan.grid, stream);
   }
   if (err != hipSuccess) return ATTN_ERR_HIP;
-  if (S > 1) {
+  if (S > 1 && !fused) {
     skv::CombineParams c{};
     c.o_part = prm.o_part;
     c.lse_part = prm.lse_part;

@@ -24,6 +24,7 @@ struct SplitParams {
   float* lse;                  // final LSE, may be null (num_splits == 1)
   float* o_part;               // [S][nrows][D] (num_splits > 1)
   float* lse_part;             // [S][nrows]    (num_splits > 1)
+  int* counters;               // [units] arrival counters, zero between calls (fused combine)
   int batch, q_len, hq, hkv, group;  // group = Hq / Hkv
   int page_size, max_pages, kv_len;
   int num_splits;

@@ -98,6 +98,20 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Partials shared between workgroups on different XCDs go straight to and
+// from memory: stores and loads carry the sc0|sc1 (system coherence) cache
+// policy, so they are written through and read past every cache, and no
+// cache has to be flushed or invalidated.
+constexpr int kSysCoherent = 17;  // CPol::SC0 | CPol::SC1
+__device__ __forceinline__ void publish(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, int(byte_off), 0,
+                                        kSysCoherent);
+}
+__device__ __forceinline__ float fetch(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_raw_buffer_load_b32(r, int(byte_off), 0, kSysCoherent));
+}
+
 // max / sum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48)
 template <bool MAX>
 __device__ __forceinline__ float across_rows(float x) {
@@ -138,8 +152,21 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   bid /= p.num_splits;
   const int rb = bid % p.row_blocks;
   bid /= p.row_blocks;
+#ifndef SKV_SWZ
+#define SKV_SWZ 0
+#endif
+#if SKV_SWZ == 1
+  // rotate the head by the sequence index so consecutive workgroups (which
+  // land on different XCDs) mix heads
+  const int b = bid / p.unit_heads;
+  const int uh = (bid % p.unit_heads + b) % p.unit_heads;
+#elif SKV_SWZ == 2
+  const int b = bid % p.batch;
+  const int uh = bid / p.batch;
+#else
   const int uh = bid % p.unit_heads;
   const int b = bid / p.unit_heads;
+#endif
   const int hq0 = uh * p.heads_per_unit;
   const int h = hq0 / p.group;
 
@@ -300,6 +327,12 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     }
   }
 
+  // partial buffers of a split call (the host keeps them below 4 GiB)
+  const __amdgpu_buffer_rsrc_t r_opart =
+      make_rsrc(p.o_part, uint32_t(min<long>((long)p.num_splits * p.nrows * D * 4, 0xFFFFFFFFl)));
+  const __amdgpu_buffer_rsrc_t r_lpart =
+      make_rsrc(p.lse_part, uint32_t(min<long>((long)p.num_splits * p.nrows * 4, 0xFFFFFFFFl)));
+
   // ---- merge the waves through LDS and write -----------------------------
   // O layout: lane l holds rows 4g..4g+3, columns 16db + n16; l is acc[DB].
   // m of row r is held by lanes with n16 == r.
@@ -351,11 +384,75 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     if (p.num_splits == 1) {
       static_cast<uint16_t*>(p.out)[nrow * D + d] = M::round(o);
       if (d == 0 && p.lse) p.lse[((long)b * p.hq + hq) * p.q_len + i] = lse;
-    } else {
-      p.o_part[((long)split * p.nrows + nrow) * D + d] = o;
-      if (d == 0) p.lse_part[(long)split * p.nrows + nrow] = lse;
+    } else {  // write-through stores: the merging workgroup may sit on another XCD
+      publish(r_opart, uint32_t(((long)split * p.nrows + nrow) * D + d) * 4u, o);
+      if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, lse);
     }
   }
+  if (p.num_splits == 1) return;
+
+  // ---- fused combine: the last split of a unit to finish merges all ------
+  // Every split writes its partials through to memory (system-coherent
+  // stores, no cache maintenance), waits until they are complete, then bumps
+  // the unit's arrival counter; the workgroup that sees S-1 arrivals before
+  // its own reads the partials back with cache-bypassing loads and merges
+  // them, writes the output and rearms the counter at zero for the next call.
+  // Each thread owns output elements and reads the partial LSE and O of
+  // kBatch splits in one round of independent loads, folding batches with
+  // the max-shifted log-sum-exp rule (running maximum, rescaled sums).
+  constexpr int kBatch = 16;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+  __syncthreads();
+  const int unit = (b * p.unit_heads + uh) * p.row_blocks + rb;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM) == p.num_splits - 1;
+  __syncthreads();
+  if (!s_last) return;
+  const int S = p.num_splits;
+  for (int t = threadIdx.x; t < rows_here * D; t += NW * 64) {
+    const int r = t / D;
+    const int d = t % D;
+    const int pr = rb * 16 + r;
+    const int i = pr / p.heads_per_unit;
+    const int hq = hq0 + pr % p.heads_per_unit;
+    const long nrow = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
+    float mx = -INFINITY, wsum = 0.f, acc_o = 0.f;  // log2 units
+    for (int sp0 = 0; sp0 < S; sp0 += kBatch) {
+      float ls[kBatch], o[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {  // unconditional loads (clamped index), no branches
+        const int sp = min(sp0 + k, S - 1);
+        ls[k] = fetch(r_lpart, uint32_t((long)sp * p.nrows + nrow) * 4u);
+        o[k] = fetch(r_opart, uint32_t(((long)sp * p.nrows + nrow) * D + d) * 4u);
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        ls[k] = sp0 + k < S ? ls[k] * kLog2e : -INFINITY;
+        bm = fmaxf(bm, ls[k]);
+      }
+      const float mn = fmaxf(mx, bm);  // stays -inf while no split had keys
+      const float alpha = mx == mn ? 1.f : fast_exp2(mx - mn);
+      wsum *= alpha;
+      acc_o *= alpha;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float w = ls[k] == -INFINITY ? 0.f : fast_exp2(ls[k] - mn);
+        wsum += w;
+        acc_o = fmaf(w, o[k], acc_o);
+      }
+      mx = mn;
+    }
+    static_cast<uint16_t*>(p.out)[nrow * D + d] = M::round(mx == -INFINITY ? 0.f : acc_o / wsum);
+    if (d == 0 && p.lse)
+      p.lse[((long)b * p.hq + hq) * p.q_len + i] =
+          mx == -INFINITY ? -INFINITY : (mx + log2f(wsum)) * kLn2;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 #ifndef SKV_MFMA_NW

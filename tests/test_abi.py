@@ -99,11 +99,11 @@ def test_plan_fields_are_consistent(lib):
     assert code == 0
     assert plan.num_splits == 14 and plan.pack_gqa == 1
     assert plan.rows_per_unit == 8 and plan.rows_per_block == 16 and plan.row_blocks == 1
-    assert plan.units == 4 * 4 and plan.grid == 16 * 14 and plan.combine == 1
+    assert plan.units == 4 * 4 and plan.grid == 16 * 14 and plan.combine == 2
     assert plan.split_keys == 16 * 74  # ceil(1024 granules / 14) = 74
     nrows = 4 * 1 * 32
     o = (14 * nrows * 128 * 4 + 255) // 256 * 256
-    assert plan.workspace_bytes == o + (14 * nrows * 4 + 255) // 256 * 256
+    assert plan.workspace_bytes == o + (14 * nrows * 4 + 255) // 256 * 256 + 256  # + counters
     # the target paged decode workload: packed, one split, no workspace
     code, plan = _plan(lib, batch=32, q_len=1, hq=32, hkv=8, max_L=1100, maxp=69)
     assert (plan.num_splits, plan.pack_gqa, plan.rows_per_block, plan.grid) == (1, 1, 16, 256)

@@ -73,7 +73,7 @@ def test_paged_gqa4_bf16_full_size_split_sweep(c3, S):
     wl, ref = c3
     case("paged bf16 B32 Hq32/Hkv8 d128, num_splits=%d" % S)
     plan = assert_paged(wl, num_splits=S, ref=ref)
-    assert plan.num_splits == S and plan.combine == 1
+    assert plan.num_splits == S and plan.combine >= 1
 
 
 def test_paged_gqa4_bf16_full_size_unpacked(c3):
@@ -198,7 +198,12 @@ def test_partials_and_combine_separately():
                            torch.bfloat16, num_splits=S)
     ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
     case("split partials S=4 read back from the workspace")
-    run_paged(wl, num_splits=S, workspace=ws)
+    out1, lse1, _ = run_paged(wl, num_splits=S, workspace=ws)
+    if plan.combine == 2:  # the fused combine leaves its arrival counters at zero
+        o_bytes = (S * 48 * 128 * 4 + 255) // 256 * 256 + (S * 48 * 4 + 255) // 256 * 256
+        assert int(ws[o_bytes:].view(torch.int32).abs().sum()) == 0
+    out2, lse2, _ = run_paged(wl, num_splits=S, workspace=ws)  # same workspace again
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
     nrows = 3 * 2 * 8
     o_gpu, l_gpu = api.workspace_partials(ws, plan, nrows, 128)
     assert plan.split_keys == oracle.split_keys_for(wl.max_seqlen_k, S)
