@@ -147,7 +147,11 @@ attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int
  *     int32 arrival counters [plan.units].  The counters must be zero
  *     before the first call that uses the workspace (fill it with zeros
  *     once); every call leaves them zero again.  Calls that share one
- *     workspace must not run concurrently.
+ *     workspace must not run concurrently.  With combine == 2 only the
+ *     partials of splits that hold keys of a sequence spanning two or more
+ *     splits are written (an empty split adds nothing to the merge; a
+ *     sequence within one split is written to out directly); the other
+ *     entries keep whatever they held.
  * The plan uses the compute-unit count of the current device. */
 attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* block_table,

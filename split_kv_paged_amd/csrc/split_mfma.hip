@@ -147,26 +147,16 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   const int n16 = lane & 15;  // S^T: query row; O: column within a 16-wide d block
   const int g = lane >> 4;    // S^T: key group (keys 4g..4g+3); O: rows 4g..4g+3
 
-  int bid = blockIdx.x;
-  const int split = bid % p.num_splits;
-  bid /= p.num_splits;
+  // Workgroups run split-major from the last split down: the last splits
+  // exist only for the longest sequences, so their work is dispatched first
+  // and the short remainder fills in behind it.
+  const int units = p.batch * p.unit_heads * p.row_blocks;
+  const int split = p.num_splits - 1 - int(blockIdx.x) / units;
+  int bid = int(blockIdx.x) % units;
   const int rb = bid % p.row_blocks;
   bid /= p.row_blocks;
-#ifndef SKV_SWZ
-#define SKV_SWZ 0
-#endif
-#if SKV_SWZ == 1
-  // rotate the head by the sequence index so consecutive workgroups (which
-  // land on different XCDs) mix heads
-  const int b = bid / p.unit_heads;
-  const int uh = (bid % p.unit_heads + b) % p.unit_heads;
-#elif SKV_SWZ == 2
-  const int b = bid % p.batch;
-  const int uh = bid / p.batch;
-#else
   const int uh = bid % p.unit_heads;
   const int b = bid / p.unit_heads;
-#endif
   const int hq0 = uh * p.heads_per_unit;
   const int h = hq0 / p.group;
 
@@ -180,8 +170,15 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       return 0;
     }
   };
-  int pages = load_pages(0);
   const int L = PAGED ? p.seqlens[b] : p.kv_len;
+  // Splits of this sequence that hold keys.  Past the last key a split has
+  // nothing to add (its LSE would be -inf, weight zero in the combine), so
+  // its workgroup leaves at once; a sequence that fits in one split is
+  // finished by split 0 alone, with no partials and no combine.
+  const int nsplit = p.num_splits == 1 ? 1 : max(1, (L + p.split_keys - 1) / p.split_keys);
+  if (split >= nsplit) return;
+  const bool direct = nsplit == 1;
+  int pages = load_pages(0);
   const int t1 = min(t0 + p.split_keys, L);
   const int n_tiles = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
@@ -381,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     const int i = pr / p.heads_per_unit;
     const int hq = hq0 + pr % p.heads_per_unit;
     const long nrow = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
-    if (p.num_splits == 1) {
+    if (direct) {
       static_cast<uint16_t*>(p.out)[nrow * D + d] = M::round(o);
       if (d == 0 && p.lse) p.lse[((long)b * p.hq + hq) * p.q_len + i] = lse;
     } else {  // write-through stores: the merging workgroup may sit on another XCD
@@ -389,12 +386,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, lse);
     }
   }
-  if (p.num_splits == 1) return;
+  if (direct) return;
 
   // ---- fused combine: the last split of a unit to finish merges all ------
-  // Every split writes its partials through to memory (system-coherent
-  // stores, no cache maintenance), waits until they are complete, then bumps
-  // the unit's arrival counter; the workgroup that sees S-1 arrivals before
+  // Every split that holds keys writes its partials through to memory
+  // (system-coherent stores, no cache maintenance), waits until they are
+  // complete, then bumps the unit's arrival counter; the workgroup that sees
+  // the other nsplit-1 arrivals before
   // its own reads the partials back with cache-bypassing loads and merges
   // them, writes the output and rearms the counter at zero for the next call.
   // Each thread owns output elements and reads the partial LSE and O of
@@ -408,10 +406,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   const int unit = (b * p.unit_heads + uh) * p.row_blocks + rb;
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_SYSTEM) == p.num_splits - 1;
+                                    __HIP_MEMORY_SCOPE_SYSTEM) == nsplit - 1;
   __syncthreads();
   if (!s_last) return;
-  const int S = p.num_splits;
+  const int S = nsplit;
   for (int t = threadIdx.x; t < rows_here * D; t += NW * 64) {
     const int r = t / D;
     const int d = t % D;

@@ -210,8 +210,24 @@ def test_partials_and_combine_separately():
     o_ref, l_ref = oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
                                                wl.cache_seqlens, "bf16", S, plan.split_keys,
                                                block=16, scale=wl.scale)
-    check_f32(o_gpu.cpu().numpy(), o_ref)
-    check_lse(l_gpu.cpu().numpy(), l_ref)
+    o_gpu, l_gpu = o_gpu.cpu().numpy(), l_gpu.cpu().numpy()
+    if plan.combine == 2:
+        # the fused path writes the partials of splits holding keys of
+        # sequences that span two or more splits; the rest add nothing
+        C = plan.split_keys
+        nsplit = np.maximum(1, -(-wl.cache_seqlens.astype(np.int64) // C))
+        seq_of_row = np.arange(nrows) // (2 * 8)  # rows ordered (b, i, hq)
+        ns = nsplit[seq_of_row]
+        written = (ns[None, :] >= 2) & (np.arange(S)[:, None] < ns[None, :])
+        assert written.any() and not written.all()
+        # what is skipped: whole sequences within one split, and empty splits
+        one_split = np.broadcast_to(ns[None, :] == 1, written.shape)
+        assert np.all(one_split[~written] | np.isneginf(l_ref[~written]))
+        check_f32(o_gpu[written], o_ref[written])
+        check_lse(l_gpu[written], l_ref[written])
+    else:
+        check_f32(o_gpu, o_ref)
+        check_lse(l_gpu, l_ref)
     case("combine kernel on the oracle's partials")
     o32 = o_ref.astype(np.float32)
     l32 = l_ref.astype(np.float32)
