@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, copy this many MiB device to device once (the "
+                         "known-size copy that scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -92,24 +95,35 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # Two HIP events on the launch stream bracket the K launches; the host
+    # enqueues faster than the GPU drains, so the launches run back to back
+    # and (end - start) / K is the average launch duration.
     K = args.steps
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev_start.record(stream)
     for i in range(K):
-        ev0[i].record(stream)
         step(i)
-        ev1[i].record(stream)
+    ev_end.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = (t1 - t0) / K
-    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+    launch_ms = ev_start.elapsed_time(ev_end) / K
     last = api.last_plan()
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     kv_bytes = wl.kv_bytes
     value = kv_bytes / wall / 1e9
-    kern_s = float(np.mean(launch_ms)) / 1e3
+    kern_s = launch_ms / 1e3
     achieved = kv_bytes / kern_s / 1e9
     qheads = wl.batch * wl.num_heads_q * wl.q_len
 
@@ -146,7 +160,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name, last.num_splits),
             "kernel_avg_us": round(kern_s * 1e6, 3),
             "kernels_per_launch": 1 + last.combine,
         },
@@ -154,6 +168,22 @@ def main():
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
+
+
+def measured_traffic(workload, num_splits):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, or None when there is none or the kernel sources changed since
+    the counters were taken."""
+    from split_kv_paged_amd import profiling
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "hbm_traffic_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    v = profiling.read_traffic(path)
+    if (v.get("workload") != workload or v.get("num_splits") != str(num_splits)
+            or v.get("source_digest") != profiling.source_digest()):
+        return None
+    return int(float(v["traffic_bytes_per_launch"]))
 
 
 def cpu_baseline(wl, budget_s):

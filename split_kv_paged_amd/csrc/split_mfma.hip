@@ -134,7 +134,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   using M = Mf<DT>;
   constexpr int KB = D / 32;        // 16x16x32 products per tile (QK)
   constexpr int DB = D / 16;        // 16x16x16 products per tile (PV)
-  constexpr int ROWB = D * 2 + 32;  // LDS bytes per staged V key row (+32 against bank clashes)
+#ifndef SKV_VSWZ
+#define SKV_VSWZ 2
+#endif
+  // LDS bytes per staged V key row: padded by 32 bytes, or unpadded with the
+  // 16-byte chunks of row r permuted by XOR with f(r) = 2(r & 3) + ((r >> 2) & 1)
+  constexpr bool kSwz = SKV_VSWZ == 2;
+  constexpr int ROWB = kSwz ? D * 2 : SKV_VSWZ == 1 ? D * 2 + 16 : D * 2 + 32;
   static_assert(D % 32 == 0, "head_dim");
 
   struct Buf {
@@ -218,8 +224,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   uint8_t* const my_v = s_buf + wave * kTile * ROWB;
   typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
   const uint32_t v_wr = uint32_t(n16 * ROWB + g * KB * 16);  // where this lane's V bytes go
+  const int f_wr = 2 * (n16 & 3) + ((n16 >> 2) & 1);            // chunk XOR of row n16
   // transposed read of d block db: lane 16g + 4i + q reads key 4g+i, d 16db + 4q .. +3
   const uint32_t v_rd = uint32_t((4 * g + ((lane & 15) >> 2)) * ROWB + (lane & 3) * 8);
+  // swizzled: row 4g+i, chunk 2db + (q>>1) lands at chunk 2(db^i) + ((q>>1)^(g&1))
+  const uint32_t v_rd_swz = uint32_t((4 * g + ((lane & 15) >> 2)) * ROWB +
+                                     (((lane & 3) >> 1) ^ (g & 1)) * 16 + (lane & 1) * 8);
+  const int i_rd = (lane & 15) >> 2;
 
   auto tile_row0 = [&](int idx, int page) -> long {
     const int tt = t0 + (wave + idx * NW) * kTile;
@@ -250,7 +261,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     // stage V (row-major, padded rows) for the transposed reads
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      *reinterpret_cast<uint4*>(my_v + v_wr + kb * 16) = bf.v[kb];
+      if constexpr (kSwz)
+        *reinterpret_cast<uint4*>(my_v + n16 * ROWB + (((g * KB + kb) ^ f_wr) * 16)) = bf.v[kb];
+      else
+        *reinterpret_cast<uint4*>(my_v + v_wr + kb * 16) = bf.v[kb];
     // S^T = K . Q^T
     f4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -287,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const s4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_ptr)(my_v + v_rd + db * 32));
+          (lds_s4_ptr)(my_v + (kSwz ? v_rd_swz + ((db ^ i_rd) * 32) : v_rd + db * 32)));
       acc[db] = M::pv(pa, __builtin_bit_cast(uint2, vt), acc[db]);
     }
     acc[DB] = M::pv(pa, make_uint2(M::kOnePair, M::kOnePair), acc[DB]);
