@@ -74,8 +74,10 @@ typedef enum { ATTN_FP16 = 0, ATTN_BF16 = 1 } attn_dtype;
  *                 slot j % page_size of page block_table[b][j / page_size]
  *   cache_seqlens int32 [batch], number of valid keys of each sequence
  *   lse           float32 [batch, num_heads_q, q_len]
- * Supported: head_dim in {64, 128}; page_size a multiple of 16; q_len >= 1
- * (no causal mask: every query row sees all L keys); any G = Hq / Hkv. */
+ * Supported: head_dim 1..256; page_size a multiple of 16; q_len >= 1 (no
+ * causal mask: every query row sees all L keys); any G = Hq / Hkv.  head_dim
+ * 32, 64, 128 and 256 move K/V in 16-byte loads; any other value is padded
+ * inside the kernel and its elements are loaded one by one (slower). */
 typedef struct {
     int32_t batch;
     int32_t q_len;
@@ -93,7 +95,8 @@ typedef struct {
  *   q, out  [num_heads_q, q_len, head_dim]
  *   k, v    [num_heads_kv, kv_len, head_dim]
  *   lse     float32 [num_heads_q, q_len]
- * Supported: head_dim in {64, 128}; any kv_len >= 0; q_len >= 1. */
+ * Supported: head_dim 1..256 (the SmallQ README's "any headDim", section
+ * 任意 headDim 支持, up to this cap); any kv_len >= 0; q_len >= 1. */
 typedef struct {
     int32_t num_heads_q;
     int32_t num_heads_kv;
@@ -109,16 +112,18 @@ typedef struct {
     int32_t num_splits;      /* S: KV ranges per (sequence, head unit)        */
     int32_t pack_gqa;        /* 1: the G query heads of a KV head share a unit */
     int32_t rows_per_unit;   /* query rows per unit: q_len*G packed, q_len not */
-    int32_t rows_per_block;  /* rows one workgroup carries (1, 2, 4 or 8)      */
+    int32_t rows_per_block;  /* packed rows one workgroup carries (16)         */
     int32_t row_blocks;      /* ceil(rows_per_unit / rows_per_block)           */
     int32_t units;           /* batch * head units * row_blocks               */
     int32_t grid;            /* workgroups of the split kernel = units * S    */
     int32_t split_granule;   /* split lengths are multiples of this many keys  */
     int32_t num_cus;         /* compute units the plan was made for           */
     int32_t combine;         /* how S > 1 partials are merged: 0 none (S = 1), */
-                             /* 1 a separate combine kernel, 2 inside the      */
-                             /* split kernel by the last split to finish       */
-    int32_t kernel;          /* kernel variant id (diagnostic)                */
+                             /* 2 inside the split kernel by the last split to */
+                             /* finish (1, a separate launch, is not used)     */
+    int32_t kernel;          /* diagnostic: 10000 (16-byte loads) or 20000     */
+                             /* (element loads) + 1000 if paged + tile head    */
+                             /* dim (32, 64, 128 or 256)                       */
     int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
     int64_t workspace_bytes; /* bytes of workspace the forward call needs     */
@@ -143,14 +148,13 @@ attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int
  *     plan.workspace_bytes (0 when S = 1, then workspace may be NULL).
  *     Layout: float32 partial outputs [S][rows][head_dim], then (at the
  *     next 256-byte boundary) float32 partial LSEs [S][rows], rows ordered
- *     (b, i, hq); when plan.combine == 2, then (next 256-byte boundary)
- *     int32 arrival counters [plan.units].  The counters must be zero
- *     before the first call that uses the workspace (fill it with zeros
- *     once); every call leaves them zero again.  Calls that share one
- *     workspace must not run concurrently.  With combine == 2 only the
- *     partials of splits that hold keys of a sequence spanning two or more
- *     splits are written (an empty split adds nothing to the merge; a
- *     sequence within one split is written to out directly); the other
+ *     (b, i, hq), then (next 256-byte boundary) int32 arrival counters
+ *     [plan.units].  The counters must be zero before the first call that
+ *     uses the workspace (fill it with zeros once); every call leaves them
+ *     zero again.  Calls that share one workspace must not run concurrently.
+ *     Only the partials of splits that hold keys of a sequence spanning two
+ *     or more splits are written (an empty split adds nothing to the merge;
+ *     a sequence within one split is written to out directly); the other
  *     entries keep whatever they held.
  * The plan uses the compute-unit count of the current device. */
 attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const void* k_cache,

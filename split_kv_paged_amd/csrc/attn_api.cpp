@@ -20,13 +20,8 @@ constexpr int kGranule = 16;        // split ranges are multiples of 16 keys
 constexpr int kMaxSplitsRule = 128; // candidate split counts tried by the rule
 constexpr int kMaxSplits = 1024;    // largest split count a caller may ask for
 constexpr int kDefaultCus = 256;    // one MI355X
-constexpr int kMaxRowsPerBlock = 8;
-constexpr int kMfmaRows = 16;
-constexpr int kMfmaKernelId = 10000;
-#ifndef SKV_USE_VALU
-#define SKV_USE_VALU 0
-#endif
-constexpr bool kUseMfma = !SKV_USE_VALU;
+constexpr int kRowsPerBlock = 16;   // packed query rows per workgroup (MFMA tile height)
+constexpr int kMaxHeadDim = 256;
 constexpr int kMaxDevices = 64;
 
 thread_local attn_plan g_last_plan;
@@ -68,11 +63,12 @@ int num_splits_rule(int64_t total_mblocks, int num_cus, int64_t num_n_blocks) {
   return 1;
 }
 
-int rows_per_block_for(int rows) {
-  if (rows <= 1) return 1;
-  if (rows <= 2) return 2;
-  if (rows <= 4) return 4;
-  return kMaxRowsPerBlock;
+// Diagnostic kernel id: 10000 (16-byte loads) or 20000 (element loads for
+// any other head_dim) + 1000 if paged + the tile head dim (32/64/128/256).
+int kernel_id(int head_dim, bool paged) {
+  const bool fast = head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
+  const int tile = head_dim <= 32 ? 32 : head_dim <= 64 ? 64 : head_dim <= 128 ? 128 : 256;
+  return (fast ? 10000 : 20000) + (paged ? 1000 : 0) + tile;
 }
 
 // Shared planner.  `dense` always packs (the dense API has no pack switch).
@@ -100,11 +96,7 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   if (splits > 1) pack = true;  // same article, section "常见坑点"
 
   const int64_t rows_per_unit = pack ? int64_t(q_len) * group : q_len;
-  // matrix-core kernel: 16 packed rows per workgroup; VALU kernel: 1..8
-  const int rpb = kUseMfma ? kMfmaRows
-                           : rows_per_block_for(int(rows_per_unit > kMaxRowsPerBlock
-                                                        ? kMaxRowsPerBlock
-                                                        : rows_per_unit));
+  const int rpb = kRowsPerBlock;
   const int64_t row_blocks = ceil_div(rows_per_unit, rpb);
   const int64_t unit_heads = pack ? hkv : hq;
   const int64_t units = batch * unit_heads * row_blocks;
@@ -117,12 +109,10 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   if (split_keys > INT32_MAX) return ATTN_ERR_SHAPE;
   int64_t ws = 0;
   if (splits > 1) {
-    ws = round_up(int64_t(splits) * nrows * head_dim * 4, 256) + round_up(int64_t(splits) * nrows * 4, 256);
-    if (kUseMfma) {
-      // the fused combine addresses the partials with 32-bit byte offsets
-      if (int64_t(splits) * nrows * head_dim * 4 >= (int64_t(1) << 32)) return ATTN_ERR_UNSUPPORTED;
-      ws += round_up(units * 4, 256);  // arrival counters
-    }
+    // the fused combine addresses the partials with 32-bit byte offsets
+    if (int64_t(splits) * nrows * head_dim * 4 >= (int64_t(1) << 32)) return ATTN_ERR_UNSUPPORTED;
+    ws = round_up(int64_t(splits) * nrows * head_dim * 4, 256) +
+         round_up(int64_t(splits) * nrows * 4, 256) + round_up(units * 4, 256);
   }
 
   std::memset(out, 0, sizeof(*out));
@@ -135,8 +125,8 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   out->grid = int(grid);
   out->split_granule = kGranule;
   out->num_cus = num_cus;
-  out->combine = splits > 1 ? (kUseMfma ? 2 : 1) : 0;
-  out->kernel = (kUseMfma ? kMfmaKernelId : 0) + skv::split_variant_id({0, head_dim, rpb, !dense});
+  out->combine = splits > 1 ? 2 : 0;
+  out->kernel = kernel_id(head_dim, !dense);
   out->split_keys = int(split_keys);
   out->workspace_bytes = ws;
   return ATTN_OK;
@@ -152,7 +142,7 @@ attn_status check_decode_shape(const attn_decode_shape* s) {
   if (s->num_heads_q % s->num_heads_kv != 0) return ATTN_ERR_SHAPE;
   if (int64_t(s->max_seqlen_k) > int64_t(s->max_pages_per_seq) * s->page_size) return ATTN_ERR_SHAPE;
   if (s->dtype != ATTN_FP16 && s->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (s->head_dim > kMaxHeadDim) return ATTN_ERR_UNSUPPORTED;
   if (s->page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
@@ -164,7 +154,7 @@ attn_status check_dense_shape(const attn_dense_shape* s) {
     return ATTN_ERR_SHAPE;
   if (s->num_heads_q % s->num_heads_kv != 0) return ATTN_ERR_SHAPE;
   if (s->dtype != ATTN_FP16 && s->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (s->head_dim > kMaxHeadDim) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -192,7 +182,7 @@ attn_status check_workspace(const attn_plan& plan, void* ws, size_t ws_bytes) {
   return ATTN_OK;
 }
 
-// Launch the split kernel (and the combine when S > 1) for a planned call.
+// Launch the split kernel (which merges the splits itself when S > 1).
 attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dtype, int head_dim,
                 void* out, float* lse, void* ws, hipStream_t stream) {
   const int S = plan.num_splits;
@@ -202,43 +192,23 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   prm.row_blocks = plan.row_blocks;
   prm.heads_per_unit = plan.pack_gqa ? prm.group : 1;
   prm.unit_heads = plan.pack_gqa ? prm.hkv : prm.hq;
+  prm.head_dim = head_dim;
   prm.out = out;
   prm.lse = lse;
-  const bool fused = plan.kernel >= kMfmaKernelId;
   if (S > 1) {
     const int64_t o_bytes = round_up(int64_t(S) * prm.nrows * head_dim * 4, 256);
     const int64_t l_bytes = round_up(int64_t(S) * prm.nrows * 4, 256);
     prm.o_part = static_cast<float*>(ws);
     prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
-    if (fused) prm.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + o_bytes + l_bytes);
+    prm.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + o_bytes + l_bytes);
   }
-  hipError_t err;
-  if (plan.kernel >= kMfmaKernelId) {
-    err = skv::launch_split_mfma(dtype, head_dim, paged, prm, plan.grid, stream);
-  } else {
-    skv::SplitVariant var{dtype, head_dim, plan.rows_per_block, paged};
-    if (!skv::split_variant_supported(var)) return ATTN_ERR_UNSUPPORTED;
-    err = skv::launch_split(var, prm, plan.grid, stream);
-  }
-  if (err != hipSuccess) return ATTN_ERR_HIP;
-  if (S > 1 && !fused) {
-    skv::CombineParams c{};
-    c.o_part = prm.o_part;
-    c.lse_part = prm.lse_part;
-    c.out = out;
-    c.lse = lse;
-    c.num_splits = S;
-    c.nrows = prm.nrows;
-    c.head_dim = head_dim;
-    if (paged) {
-      c.q_len = prm.q_len;
-      c.heads = prm.hq;
-    } else {  // dense rows (hq, i): batch = Hq, heads = 1
-      c.q_len = prm.q_len;
-      c.heads = 1;
-    }
-    if (skv::launch_combine(dtype, c, stream) != hipSuccess) return ATTN_ERR_HIP;
-  }
+  // Unsplit paged calls whose grid needs more than one round run the
+  // sequences longest first.  (With splits the split-major order already
+  // puts the long sequences' work first, and ranking in every workgroup,
+  // empty ones included, costs more than it saves.)
+  prm.by_length = paged && S == 1 && prm.batch <= skv::kMaxOrderBatch && plan.grid > plan.num_cus;
+  if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
   g_last_plan = plan;
   g_have_last = true;
   return ATTN_OK;

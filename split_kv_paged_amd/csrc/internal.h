@@ -27,6 +27,7 @@ struct SplitParams {
   int* counters;               // [units] arrival counters, zero between calls (fused combine)
   int batch, q_len, hq, hkv, group;  // group = Hq / Hkv
   int page_size, max_pages, kv_len;
+  int head_dim;        // elements per row of q, k, v and out
   int num_splits;
   int split_keys;      // keys per split (multiple of 16); split s = [s*C, (s+1)*C)
   int rows;            // valid rows per unit (q_len * heads_per_unit)
@@ -36,7 +37,10 @@ struct SplitParams {
   int nrows;           // batch * q_len * Hq
   int n_sb, n_si, n_sh;
   float scale_log2;    // softmax scale * log2(e)
+  int by_length;       // paged: run sequences longest first (batch <= kMaxOrderBatch)
 };
+
+constexpr int kMaxOrderBatch = 1024;
 
 struct CombineParams {
   const float* o_part;
@@ -50,20 +54,10 @@ struct CombineParams {
   int q_len, heads;
 };
 
-// Kernel variant selector: dtype (0 fp16, 1 bf16), head_dim, rows per block.
-struct SplitVariant {
-  int dtype;
-  int head_dim;
-  int rows_per_block;
-  bool paged;
-};
-
-hipError_t launch_split(const SplitVariant& v, const SplitParams& p, int grid, hipStream_t s);
-// matrix-core variant: 16 packed rows per workgroup, head_dim 64 or 128
-hipError_t launch_split_mfma(int dtype, int head_dim, bool paged, const SplitParams& p, int grid,
+// Split kernel (split_mfma.hip): 16 packed rows per workgroup, fused
+// combine when num_splits > 1; p.head_dim in [1, 256].
+hipError_t launch_split_mfma(int dtype, bool paged, const SplitParams& p, int grid,
                              hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t s);
-bool split_variant_supported(const SplitVariant& v);
-int split_variant_id(const SplitVariant& v);
 
 }  // namespace skv

@@ -1,7 +1,11 @@
 // split_mfma.hip -- split-KV decode / small-query attention on gfx950 matrix cores.
 //
-// Same work decomposition, split ranges, online softmax and epilogue as the
-// VALU kernel (split_kernel.hip); only the two contractions move to MFMA:
+// Work unit: (sequence, head unit, block of 16 packed query rows, split).  A
+// head unit is one KV head with its G query heads packed into the rows
+// (pack_gqa) or one query head.  One workgroup per unit; its waves take the
+// 16-key tiles of the split's key range round-robin, each with its own online
+// softmax state, and merge through LDS at the end.  The two contractions run
+// on the matrix cores:
 //
 //   S^T (16 keys x 16 rows) = K (16 x D) . Q^T (D x 16)
 //       v_mfma_f32_16x16x32_{bf16,f16}, D/32 instructions per 16-key tile.
@@ -17,6 +21,13 @@
 //       the unrounded probabilities.
 //       The V tile is staged in LDS by each wave and read back with
 //       ds_read_b64_tr_b16, which delivers the key-major B operand.
+//
+// K and V tiles move with 16-byte buffer loads into a ring of NBUF register
+// buffers: the loads of tile n+NBUF-1 are issued before tile n is computed.
+// A buffer descriptor ends at the split's last key, so keys past it (another
+// split, the poisoned tail of a page, the end of a dense tensor) read as zero
+// without a fault.  The physical page of each tile comes from the block
+// table, 64 tiles' worth per vector load, broadcast with readlane.
 //
 // Packed query rows beyond the unit's real rows are zero; their lanes do the
 // same (SIMD) work and are never written.  A unit carries at most 16 rows.
@@ -96,6 +107,12 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
 }
 
+// a 16-bit element (zero-extended); offsets past the descriptor's range read 0
+__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, int voffset) {
+  return uint32_t(__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voffset, 0, 0)));
+}
+constexpr int kPastEnd = 0x7FFFFFF0;  // beyond any tile's range (tiles are < 2 GiB)
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Partials shared between workgroups on different XCDs go straight to and
@@ -129,19 +146,25 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
                             __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, x)));
 }
 
-template <int DT, int D, int NW, int NBUF, bool PAGED>
+// D is the head dimension the tiles are built for (32, 64, 128 or 256); the
+// real one, p.head_dim <= D, may be any value.  With GEN false every key row
+// is D elements of 16-byte aligned memory and moves in 16-byte loads; with GEN
+// true (any other head_dim, the dense path's tails) each element is loaded on
+// its own and columns past p.head_dim read as zero, so they add nothing to the
+// scores and produce output columns that are never stored (the SmallQ README,
+// section "任意 headDim 支持": pad inside, store only the real columns).
+template <int DT, int D, int NW, int NBUF, bool PAGED, bool GEN>
 __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
   using M = Mf<DT>;
   constexpr int KB = D / 32;        // 16x16x32 products per tile (QK)
   constexpr int DB = D / 16;        // 16x16x16 products per tile (PV)
-#ifndef SKV_VSWZ
-#define SKV_VSWZ 2
-#endif
-  // LDS bytes per staged V key row: padded by 32 bytes, or unpadded with the
-  // 16-byte chunks of row r permuted by XOR with f(r) = 2(r & 3) + ((r >> 2) & 1)
-  constexpr bool kSwz = SKV_VSWZ == 2;
-  constexpr int ROWB = kSwz ? D * 2 : SKV_VSWZ == 1 ? D * 2 + 16 : D * 2 + 32;
+  // LDS bytes per staged V key row: unpadded with the 16-byte chunks of row
+  // r permuted by XOR with f(r) = 2(r & 3) + ((r >> 2) & 1) (needs 8 chunks
+  // a row), else padded by 32 bytes against bank clashes
+  constexpr bool kSwz = D >= 64;
+  constexpr int ROWB = kSwz ? D * 2 : D * 2 + 32;
   static_assert(D % 32 == 0, "head_dim");
+  const int hd = GEN ? p.head_dim : D;  // elements per key / query / output row
 
   struct Buf {
     uint4 k[KB];
@@ -156,13 +179,33 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // Workgroups run split-major from the last split down: the last splits
   // exist only for the longest sequences, so their work is dispatched first
   // and the short remainder fills in behind it.
+  // When the grid takes more than one round of workgroups, the sequences
+  // also run longest first within each split (a longest-processing-time
+  // order): every workgroup ranks the batch by length, ties by index.
   const int units = p.batch * p.unit_heads * p.row_blocks;
   const int split = p.num_splits - 1 - int(blockIdx.x) / units;
   int bid = int(blockIdx.x) % units;
   const int rb = bid % p.row_blocks;
   bid /= p.row_blocks;
   const int uh = bid % p.unit_heads;
-  const int b = bid / p.unit_heads;
+  int b = bid / p.unit_heads;
+  if (PAGED && p.by_length) {
+    __shared__ int s_len[kMaxOrderBatch];
+    __shared__ int s_seq;
+    for (int i = threadIdx.x; i < p.batch; i += NW * 64) s_len[i] = p.seqlens[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < p.batch; i += NW * 64) {
+      const int li = s_len[i];
+      int rank = 0;
+      for (int j = 0; j < p.batch; ++j) {
+        const int lj = s_len[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+      if (rank == b) s_seq = i;
+    }
+    __syncthreads();
+    b = s_seq;
+  }
   const int hq0 = uh * p.heads_per_unit;
   const int h = hq0 / p.group;
 
@@ -200,9 +243,25 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       const int hq = hq0 + rowq % p.heads_per_unit;
       n = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
     }
-    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * D);
+    if constexpr (GEN) {
+      const uint16_t* qr = static_cast<const uint16_t*>(p.q) + n * hd;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qb[kb] = real ? qp[g * KB + kb] : make_uint4(0, 0, 0, 0);
+      for (int kb = 0; kb < KB; ++kb) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c0 = (g * KB + kb) * 8 + 2 * e;
+          const uint32_t lo = (real && c0 < hd) ? qr[c0] : 0u;
+          const uint32_t hi = (real && c0 + 1 < hd) ? qr[c0 + 1] : 0u;
+          w[e] = lo | (hi << 16);
+        }
+        qb[kb] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * D);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qb[kb] = real ? qp[g * KB + kb] : make_uint4(0, 0, 0, 0);
+    }
   }
 
   f4_t acc[DB + 1];  // O blocks; acc[DB] is the all-ones block: column sums = l
@@ -211,7 +270,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   float m = -INFINITY;  // reference max of row n16 (S^T layout), log2 units
   float l32 = 0.f;      // float32 sum of this lane's probabilities (row n16)
 
-  const long row_stride = PAGED ? (long)p.hkv * D : (long)D;
+  const long row_stride = PAGED ? (long)p.hkv * hd : (long)hd;
   const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.k);
   const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(p.v);
   const int voff = int((n16 * row_stride + g * KB * 8) * 2);  // key n16, bytes [16*KB*g, +16*KB)
@@ -235,9 +294,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   auto tile_row0 = [&](int idx, int page) -> long {
     const int tt = t0 + (wave + idx * NW) * kTile;
     if constexpr (PAGED) {
-      return ((long)page * p.page_size + tt % p.page_size) * p.hkv * D + (long)h * D;
+      return ((long)page * p.page_size + tt % p.page_size) * p.hkv * hd + (long)h * hd;
     } else {
-      return ((long)h * p.kv_len + tt) * D;
+      return ((long)h * p.kv_len + tt) * hd;
     }
   };
 
@@ -248,10 +307,29 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     const uint32_t bytes = uint32_t(min(kTile, t1 - tt) * row_stride * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0, bytes);
+    if constexpr (GEN) {
+      // element loads; a column past the head dim gets an offset past the
+      // descriptor's range, which reads as zero
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bf.k[kb] = load16(rk, voff + kb * 16);
-      bf.v[kb] = load16(rv, voff + kb * 16);
+      for (int kb = 0; kb < KB; ++kb) {
+        uint32_t wk[4], wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c0 = (g * KB + kb) * 8 + 2 * e;
+          const int o0 = c0 < hd ? int((n16 * row_stride + c0) * 2) : kPastEnd;
+          const int o1 = c0 + 1 < hd ? int((n16 * row_stride + c0 + 1) * 2) : kPastEnd;
+          wk[e] = load2(rk, o0) | (load2(rk, o1) << 16);
+          wv[e] = load2(rv, o0) | (load2(rv, o1) << 16);
+        }
+        bf.k[kb] = make_uint4(wk[0], wk[1], wk[2], wk[3]);
+        bf.v[kb] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        bf.k[kb] = load16(rk, voff + kb * 16);
+        bf.v[kb] = load16(rv, voff + kb * 16);
+      }
     }
   };
 
@@ -314,7 +392,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       process_tile(bf, tt, std::false_type{});
   };
 
-  // ---- main loop: NBUF tiles in a register ring (see split_kernel.hip) ---
+  // ---- main loop: NBUF tiles in a register ring --------------------------
   for (int cb = 0; cb < my_tiles; cb += 64) {
     if (cb > 0) pages = load_pages(cb);
     const int n = min(64, my_tiles - cb);
@@ -340,7 +418,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 
   // partial buffers of a split call (the host keeps them below 4 GiB)
   const __amdgpu_buffer_rsrc_t r_opart =
-      make_rsrc(p.o_part, uint32_t(min<long>((long)p.num_splits * p.nrows * D * 4, 0xFFFFFFFFl)));
+      make_rsrc(p.o_part, uint32_t(min<long>((long)p.num_splits * p.nrows * hd * 4, 0xFFFFFFFFl)));
   const __amdgpu_buffer_rsrc_t r_lpart =
       make_rsrc(p.lse_part, uint32_t(min<long>((long)p.num_splits * p.nrows * 4, 0xFFFFFFFFl)));
 
@@ -370,9 +448,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   }
   __syncthreads();
 
-  for (int t = threadIdx.x; t < rows_here * D; t += NW * 64) {
-    const int r = t / D;
-    const int d = t % D;
+  for (int t = threadIdx.x; t < rows_here * hd; t += NW * 64) {
+    const int r = t / hd;
+    const int d = t % hd;
     const int pr = rb * 16 + r;
     float Mx = -INFINITY;
 #pragma unroll
@@ -393,10 +471,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     const int hq = hq0 + pr % p.heads_per_unit;
     const long nrow = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
     if (direct) {
-      static_cast<uint16_t*>(p.out)[nrow * D + d] = M::round(o);
+      static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(o);
       if (d == 0 && p.lse) p.lse[((long)b * p.hq + hq) * p.q_len + i] = lse;
     } else {  // write-through stores: the merging workgroup may sit on another XCD
-      publish(r_opart, uint32_t(((long)split * p.nrows + nrow) * D + d) * 4u, o);
+      publish(r_opart, uint32_t(((long)split * p.nrows + nrow) * hd + d) * 4u, o);
       if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, lse);
     }
   }
@@ -424,9 +502,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   __syncthreads();
   if (!s_last) return;
   const int S = nsplit;
-  for (int t = threadIdx.x; t < rows_here * D; t += NW * 64) {
-    const int r = t / D;
-    const int d = t % D;
+  for (int t = threadIdx.x; t < rows_here * hd; t += NW * 64) {
+    const int r = t / hd;
+    const int d = t % hd;
     const int pr = rb * 16 + r;
     const int i = pr / p.heads_per_unit;
     const int hq = hq0 + pr % p.heads_per_unit;
@@ -438,7 +516,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       for (int k = 0; k < kBatch; ++k) {  // unconditional loads (clamped index), no branches
         const int sp = min(sp0 + k, S - 1);
         ls[k] = fetch(r_lpart, uint32_t((long)sp * p.nrows + nrow) * 4u);
-        o[k] = fetch(r_opart, uint32_t(((long)sp * p.nrows + nrow) * D + d) * 4u);
+        o[k] = fetch(r_opart, uint32_t(((long)sp * p.nrows + nrow) * hd + d) * 4u);
       }
       float bm = -INFINITY;
 #pragma unroll
@@ -458,7 +536,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       }
       mx = mn;
     }
-    static_cast<uint16_t*>(p.out)[nrow * D + d] = M::round(mx == -INFINITY ? 0.f : acc_o / wsum);
+    static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(mx == -INFINITY ? 0.f : acc_o / wsum);
     if (d == 0 && p.lse)
       p.lse[((long)b * p.hq + hq) * p.q_len + i] =
           mx == -INFINITY ? -INFINITY : (mx + log2f(wsum)) * kLn2;
@@ -467,41 +545,46 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-#ifndef SKV_MFMA_NW
-#define SKV_MFMA_NW 8
-#endif
-#ifndef SKV_MFMA_NBUF
-#define SKV_MFMA_NBUF 2
-#endif
-
-template <int DT, int D, bool PAGED>
+// Waves per workgroup and tiles in flight per wave: 8 and 2 up to D = 128;
+// at D = 256 the accumulators and tiles leave room for one tile in flight
+// and the merge buffer for 4 waves; element loads at D = 128 also keep one
+// tile in flight (two would spill).
+template <int DT, int D, bool PAGED, bool GEN>
 hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
-  constexpr int NW = SKV_MFMA_NW;
-  constexpr int NBUF = SKV_MFMA_NBUF;
-  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED>), dim3(grid), dim3(NW * 64), 0, s,
-                     p);
+  constexpr int NW = D <= 128 ? 8 : 4;
+  constexpr int NBUF = (D > 128 || (GEN && D == 128)) ? 1 : 2;
+  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN>), dim3(grid), dim3(NW * 64),
+                     0, s, p);
   return hipGetLastError();
 }
 
 template <int DT, bool PAGED>
-hipError_t launch_mfma_dt(int head_dim, const SplitParams& p, int grid, hipStream_t s) {
-  switch (head_dim) {
-    case 64: return launch_mfma_d<DT, 64, PAGED>(p, grid, s);
-    case 128: return launch_mfma_d<DT, 128, PAGED>(p, grid, s);
+hipError_t launch_mfma_dt(const SplitParams& p, int grid, hipStream_t s) {
+  const int d = p.head_dim;
+  const bool gen = !(d == 32 || d == 64 || d == 128 || d == 256);
+  if (gen) {
+    if (d <= 32) return launch_mfma_d<DT, 32, PAGED, true>(p, grid, s);
+    if (d <= 64) return launch_mfma_d<DT, 64, PAGED, true>(p, grid, s);
+    if (d <= 128) return launch_mfma_d<DT, 128, PAGED, true>(p, grid, s);
+    if (d <= 256) return launch_mfma_d<DT, 256, PAGED, true>(p, grid, s);
+    return hipErrorInvalidValue;
+  }
+  switch (d) {
+    case 32: return launch_mfma_d<DT, 32, PAGED, false>(p, grid, s);
+    case 64: return launch_mfma_d<DT, 64, PAGED, false>(p, grid, s);
+    case 128: return launch_mfma_d<DT, 128, PAGED, false>(p, grid, s);
+    case 256: return launch_mfma_d<DT, 256, PAGED, false>(p, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_split_mfma(int dtype, int head_dim, bool paged, const SplitParams& p, int grid,
-                             hipStream_t s) {
+hipError_t launch_split_mfma(int dtype, bool paged, const SplitParams& p, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (paged)
-    return dtype == 1 ? launch_mfma_dt<1, true>(head_dim, p, grid, s)
-                      : launch_mfma_dt<0, true>(head_dim, p, grid, s);
-  return dtype == 1 ? launch_mfma_dt<1, false>(head_dim, p, grid, s)
-                    : launch_mfma_dt<0, false>(head_dim, p, grid, s);
+    return dtype == 1 ? launch_mfma_dt<1, true>(p, grid, s) : launch_mfma_dt<0, true>(p, grid, s);
+  return dtype == 1 ? launch_mfma_dt<1, false>(p, grid, s) : launch_mfma_dt<0, false>(p, grid, s);
 }
 
 }  // namespace skv

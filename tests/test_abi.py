@@ -116,10 +116,21 @@ def test_plan_fields_are_consistent(lib):
     assert plan.rows_per_unit == 2 and plan.units == 2 * 8
 
 
+def test_plan_kernel_ids_name_the_tile_and_load_path(lib):
+    for d, want in [(64, 11064), (128, 11128), (32, 11032), (256, 11256), (96, 21128),
+                    (1, 21032), (200, 21256), (33, 21064)]:
+        code, plan = _plan(lib, batch=2, q_len=1, hq=8, hkv=2, max_L=512, maxp=32, d=d)
+        assert code == 0 and plan.kernel == want, (d, plan.kernel)
+    shape = L.DenseShape(8, 2, 1, 512, 80, 0)
+    plan = L.Plan()
+    assert lib.attn_dense_plan(ctypes.byref(shape), 0, 0, ctypes.byref(plan)) == 0
+    assert plan.kernel == 20128
+
+
 @pytest.mark.parametrize("field,value,want", [
     ("batch", -1, "ATTN_ERR_SHAPE"), ("q_len", 0, "ATTN_ERR_SHAPE"),
     ("hq", 0, "ATTN_ERR_SHAPE"), ("hkv", 3, "ATTN_ERR_SHAPE"),
-    ("d", 96, "ATTN_ERR_UNSUPPORTED"), ("d", 0, "ATTN_ERR_SHAPE"),
+    ("d", 257, "ATTN_ERR_UNSUPPORTED"), ("d", 0, "ATTN_ERR_SHAPE"),
     ("page", 0, "ATTN_ERR_SHAPE"), ("page", 8, "ATTN_ERR_UNSUPPORTED"),
     ("maxp", 0, "ATTN_ERR_SHAPE"), ("max_L", 8193, "ATTN_ERR_SHAPE"),
     ("max_L", -5, "ATTN_ERR_SHAPE"), ("dt", 2, "ATTN_ERR_UNSUPPORTED"),
@@ -151,7 +162,7 @@ def test_dense_plan(lib):
     for bad, want in [(L.DenseShape(8, 3, 1, 512, 64, 0), "ATTN_ERR_SHAPE"),
                       (L.DenseShape(8, 2, 0, 512, 64, 0), "ATTN_ERR_SHAPE"),
                       (L.DenseShape(8, 2, 1, -1, 64, 0), "ATTN_ERR_SHAPE"),
-                      (L.DenseShape(8, 2, 1, 512, 80, 0), "ATTN_ERR_UNSUPPORTED")]:
+                      (L.DenseShape(8, 2, 1, 512, 300, 0), "ATTN_ERR_UNSUPPORTED")]:
         assert L.STATUS[lib.attn_dense_plan(ctypes.byref(bad), 0, 0, ctypes.byref(plan))] == want
 
 
@@ -172,7 +183,7 @@ def test_forward_validation_before_any_device_call(lib):
                                         None, None, 0, None)] == "ATTN_ERR_ALIGN"
     assert L.STATUS[lib.attn_decode_fwd(ctypes.byref(good), a, a, a, a, a, 0, -1,
                                         float("nan"), a, None, None, 0, None)] == "ATTN_ERR_ARG"
-    dshape = L.DenseShape(8, 2, 1, 512, 96, 0)
+    dshape = L.DenseShape(8, 2, 1, 512, 257, 0)
     assert L.STATUS[lib.attn_dense_fwd(ctypes.byref(dshape), a, a, a, 0, 0.0, a, None, None, 0,
                                        None)] == "ATTN_ERR_UNSUPPORTED"
     assert L.STATUS[lib.attn_combine_fwd(0, 1, 1, 8, 128, 1, a, a, a, None, None)] == \

@@ -3,7 +3,7 @@
 Every test prints the case it is about to run (flushed) before its first
 GPU call.  Full-size cases use the five named workloads; small cases span
 several 16-key tiles with ragged tails, GQA 1/2/4/8, q_len up to 8 (row
-blocks), head_dim 64/128, both dtypes, page sizes 16/32, empty sequences
+blocks), head_dim 1..256, both dtypes, page sizes 16/32/48, empty sequences
 and NaN-poisoned slots outside the valid keys.
 """
 import sys
@@ -140,6 +140,37 @@ def test_smallq_mha_fp16(kv_len):
         check_out(bits_of(out), ref_o, "fp16")
         check_lse(lse.cpu().numpy(), ref_l)
     print("  planner S=%d" % plan.num_splits, flush=True)
+
+
+# ---------------------------------------------------------- any head_dim ----
+
+ODD_DIMS = [1, 7, 16, 24, 33, 48, 80, 96, 100, 112, 130, 160, 192, 200, 255, 256, 32]
+
+
+@pytest.mark.parametrize("d", ODD_DIMS)
+def test_dense_any_head_dim(d):
+    """Row a11's arbitrary head dim: padded tiles, element loads, masked
+    stores (head dims 32/64/128/256 take the 16-byte path)."""
+    dt = "bf16" if d % 2 else "fp16"
+    wl = W.make_dense(900 + d, dt, 8, 2, 3, 301, d)
+    ref_o, ref_l = oracle.dense_attention(wl.q, wl.k, wl.v, dt, scale=wl.scale)
+    q, k, v = to_dev(wl.q, dt), to_dev(wl.k, dt), to_dev(wl.v, dt)
+    for S in (1, 4):
+        case("dense %s Hq8/Hkv2 qLen3 kvLen301 head_dim=%d num_splits=%d" % (dt, d, S))
+        out, lse = api.dense_fwd(q, k, v, num_splits=S)
+        torch.cuda.synchronize()
+        check_out(bits_of(out), ref_o, dt)
+        check_lse(lse.cpu().numpy(), ref_l)
+        assert api.last_plan().kernel % 1000 >= d
+
+
+@pytest.mark.parametrize("d", [32, 80, 96, 256])
+def test_paged_any_head_dim(d):
+    wl = W.make_paged(950 + d, "bf16", 3, 2, 8, 2, d, 16, [5, 130, 47], spare_pages=2)
+    ref = oracle_paged(wl)
+    for S in (1, 3):
+        case("paged bf16 B3 q2 Hq8/Hkv2 head_dim=%d S=%d" % (d, S))
+        assert_paged(wl, num_splits=S, ref=ref)
 
 
 # ------------------------------------------------------------- small shapes --
