@@ -29,9 +29,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3",
-                    choices=["c3", "c4", "c5"],
+                    choices=["c1", "c2", "c3", "c4", "c5"],
                     help="c3: paged bf16 B32 Hq32/Hkv8 d128 L~1000 (default); "
-                         "c4: B4 Hq32/Hkv4 L16384; c5: ragged fp16 B128 d64")
+                         "c4: B4 Hq32/Hkv4 L16384; c5: ragged fp16 B128 d64; "
+                         "c1: dense fp16 Hq8/Hkv2 d64 kvLen512; "
+                         "c2: dense fp16 MHA 32 heads qLen4 d128 (--kv-len)")
+    ap.add_argument("--kv-len", type=int, default=4096, help="c2 only")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = planner")
     ap.add_argument("--pools", type=int, default=4, help="KV pool copies rotated over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -43,9 +46,12 @@ def parse():
     return ap.parse_args()
 
 
-def make_workload(name):
+def make_workload(name, kv_len=4096):
     from split_kv_paged_amd import workloads as W
-    return {"c3": W.c3_paged_gqa4, "c4": W.c4_long, "c5": W.c5_ragged}[name]()
+    if name == "c2":
+        return W.c2_smallq(kv_len)
+    return {"c1": W.c1_dense_decode, "c3": W.c3_paged_gqa4, "c4": W.c4_long,
+            "c5": W.c5_ragged}[name]()
 
 
 def main():
@@ -59,7 +65,8 @@ def main():
 
     from split_kv_paged_amd import api
 
-    wl = make_workload(args.workload)
+    wl = make_workload(args.workload, args.kv_len)
+    dense = args.workload in ("c1", "c2")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
@@ -68,25 +75,32 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
 
     q = dev16(wl.q)
-    pools = [(dev16(wl.k_cache), dev16(wl.v_cache)) for _ in range(max(1, args.pools))]
-    bt = torch.from_numpy(wl.block_table).to(dev)
-    sl = torch.from_numpy(wl.cache_seqlens).to(dev)
-    max_L = wl.max_seqlen_k
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    plan = api.decode_plan(wl.batch, wl.q_len, wl.num_heads_q, wl.num_heads_kv, wl.head_dim,
-                           wl.page_size, wl.block_table.shape[1], max_L, tdt,
-                           num_splits=args.num_splits, num_cus=cus)
-    out = torch.empty_like(q)
-    lse = torch.empty((wl.batch, wl.num_heads_q, wl.q_len), dtype=torch.float32, device=dev)
-    ws = (torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
-          if plan.workspace_bytes else None)
     stream = torch.cuda.current_stream(dev)
-
+    out = torch.empty_like(q)
     # one prepared call per KV pool: the per-step host work is a single call
     # into the C ABI (which still plans and validates every time)
-    calls = [api.PreparedDecode(q, kc, vc, bt, sl, num_splits=args.num_splits,
-                                softmax_scale=wl.scale, max_seqlen_k=max_L, out=out, lse=lse,
-                                workspace=ws, stream=stream) for kc, vc in pools]
+    if dense:
+        pools = [(dev16(wl.k), dev16(wl.v)) for _ in range(max(1, args.pools))]
+        lse = torch.empty((wl.num_heads_q, wl.q_len), dtype=torch.float32, device=dev)
+        first = api.PreparedDense(q, pools[0][0], pools[0][1], num_splits=args.num_splits,
+                                  softmax_scale=wl.scale, out=out, lse=lse, stream=stream)
+        calls = [first] + [api.PreparedDense(q, k, v, num_splits=args.num_splits,
+                                             softmax_scale=wl.scale, out=out, lse=lse,
+                                             workspace=first.workspace, stream=stream)
+                           for k, v in pools[1:]]
+    else:
+        pools = [(dev16(wl.k_cache), dev16(wl.v_cache)) for _ in range(max(1, args.pools))]
+        bt = torch.from_numpy(wl.block_table).to(dev)
+        sl = torch.from_numpy(wl.cache_seqlens).to(dev)
+        lse = torch.empty((wl.batch, wl.num_heads_q, wl.q_len), dtype=torch.float32, device=dev)
+        first = api.PreparedDecode(q, pools[0][0], pools[0][1], bt, sl,
+                                   num_splits=args.num_splits, softmax_scale=wl.scale,
+                                   max_seqlen_k=wl.max_seqlen_k, out=out, lse=lse, stream=stream)
+        calls = [first] + [api.PreparedDecode(q, kc, vc, bt, sl, num_splits=args.num_splits,
+                                              softmax_scale=wl.scale,
+                                              max_seqlen_k=wl.max_seqlen_k, out=out, lse=lse,
+                                              workspace=first.workspace, stream=stream)
+                           for kc, vc in pools[1:]]
 
     def step(i):
         calls[i % len(calls)]()
@@ -125,7 +139,20 @@ def main():
     value = kv_bytes / wall / 1e9
     kern_s = launch_ms / 1e3
     achieved = kv_bytes / kern_s / 1e9
-    qheads = wl.batch * wl.num_heads_q * wl.q_len
+    batch = 1 if dense else wl.batch
+    qheads = batch * wl.num_heads_q * wl.q_len
+    if dense:
+        config = {"workload": wl.name, "layout": "dense [H, len, d]", "num_heads_q":
+                  wl.num_heads_q, "num_heads_kv": wl.num_heads_kv, "q_len": wl.q_len,
+                  "kv_len": wl.kv_len, "head_dim": wl.head_dim}
+    else:
+        config = {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len,
+                  "num_heads_q": wl.num_heads_q, "num_heads_kv": wl.num_heads_kv,
+                  "head_dim": wl.head_dim, "page_size": wl.page_size,
+                  "kv_tokens": int(wl.cache_seqlens.sum())}
+    config.update({"kv_bytes": kv_bytes, "num_splits": last.num_splits,
+                   "pack_gqa": last.pack_gqa, "grid": last.grid, "kv_pools": len(pools),
+                   "accumulate": "f32"})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -143,15 +170,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded N(0,1) bf16 K/V/Q, shuffled page table)",
-        "config": {
-            "workload": wl.name, "batch": wl.batch, "q_len": wl.q_len,
-            "num_heads_q": wl.num_heads_q, "num_heads_kv": wl.num_heads_kv,
-            "head_dim": wl.head_dim, "page_size": wl.page_size,
-            "kv_tokens": int(wl.cache_seqlens.sum()), "kv_bytes": kv_bytes,
-            "num_splits": last.num_splits, "pack_gqa": last.pack_gqa,
-            "grid": last.grid, "kv_pools": len(pools), "accumulate": "f32",
-        },
+        "data": "synthetic (seeded N(0,1) %s Q/K/V%s)" % (
+            wl.dtype, "" if dense else ", shuffled page table"),
+        "config": config,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "query_heads_per_s": round(qheads / wall, 1),
         "roofline": {
@@ -193,21 +214,26 @@ def cpu_baseline(wl, budget_s):
 
     import oracle
     threads = oracle.default_threads()
+    dense = not hasattr(wl, "block_table")
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.cache_seqlens,
-                               wl.dtype, scale=wl.scale, nthreads=threads)
+        if dense:
+            oracle.dense_attention(wl.q, wl.k, wl.v, wl.dtype, scale=wl.scale, nthreads=threads)
+        else:
+            oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                   wl.cache_seqlens, wl.dtype, scale=wl.scale, nthreads=threads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s or len(times) >= 20:
             break
     t = float(np.median(times))
+    rows = wl.q_len * wl.num_heads_q * (1 if dense else wl.batch)
+    keys = wl.kv_len if dense else int(wl.cache_seqlens.sum())
     return {"value": round(wl.kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "whole workload (%d query rows, %d keys), %d repetitions, median %.3f s"
-                      % (wl.batch * wl.q_len * wl.num_heads_q, int(wl.cache_seqlens.sum()),
-                         len(times), t)}
+                      % (rows, keys, len(times), t)}
 
 
 if __name__ == "__main__":

@@ -245,3 +245,48 @@ class PreparedDecode:
         if code:
             _L.check("attn_decode_fwd", code)
         return self.out, self.lse
+
+
+class PreparedDense:
+    """A dense call with its arguments marshalled once, for tight loops (see
+    PreparedDecode); each call re-enters attn_dense_fwd with optionally
+    swapped K/V pointers."""
+
+    def __init__(self, q, k, v, num_splits=0, softmax_scale=None, out=None, lse=None,
+                 workspace=None, stream=None):
+        _need(q.dtype in _DT and k.dtype == q.dtype and v.dtype == q.dtype,
+              "q, k, v must share fp16 or bf16")
+        dev = _check_dev(q, k, v, out, lse, workspace)
+        hq, qlen, d = q.shape
+        hkv, kvlen, d2 = k.shape
+        _need(d2 == d and tuple(v.shape) == tuple(k.shape), "k/v shapes")
+        self.shape = _L.DenseShape(hq, hkv, qlen, kvlen, d, _DT[q.dtype])
+        self.lib = _L.load()
+        plan = _L.Plan()
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        _L.check("attn_dense_plan", self.lib.attn_dense_plan(
+            ctypes.byref(self.shape), num_splits, cus, ctypes.byref(plan)))
+        self.plan = plan
+        self.out = out if out is not None else torch.empty_like(q)
+        self.lse = lse if lse is not None else torch.empty((hq, qlen), dtype=torch.float32,
+                                                           device=dev)
+        if workspace is None and plan.workspace_bytes > 0:
+            workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self._keep = (q, k, v)
+        self.args = [ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), int(num_splits),
+                     float(softmax_scale) if softmax_scale else 0.0, _ptr(self.out),
+                     _ptr(self.lse), _ptr(workspace),
+                     workspace.numel() if workspace is not None else 0, _stream(dev, stream)]
+        self.fn = self.lib.attn_dense_fwd
+
+    def __call__(self, k=None, v=None):
+        a = self.args
+        if k is not None:
+            a = list(a)
+            a[2] = ctypes.c_void_p(k.data_ptr())
+            a[3] = ctypes.c_void_p(v.data_ptr())
+        code = self.fn(*a)
+        if code:
+            _L.check("attn_dense_fwd", code)
+        return self.out, self.lse
