@@ -50,14 +50,16 @@ def _load(path=None):
         P = ctypes.c_void_p
         I = ctypes.c_int
         D = ctypes.c_double
-        lib.oracle_paged_attention.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, D, I, P, P]
+        lib.oracle_paged_attention.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, D, I, I, P,
+                                               P]
         lib.oracle_paged_attention.restype = I
-        lib.oracle_dense_attention.argtypes = [I, I, I, I, I, I, P, P, P, D, I, P, P]
+        lib.oracle_dense_attention.argtypes = [I, I, I, I, I, I, P, P, P, D, I, I, P, P]
         lib.oracle_dense_attention.restype = I
         lib.oracle_paged_split_partials.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, D, I, I,
-                                                    I, I, P, P]
+                                                    I, I, I, P, P]
         lib.oracle_paged_split_partials.restype = I
-        lib.oracle_dense_split_partials.argtypes = [I, I, I, I, I, I, P, P, P, D, I, I, I, I, P, P]
+        lib.oracle_dense_split_partials.argtypes = [I, I, I, I, I, I, P, P, P, D, I, I, I, I, I, P,
+                                                    P]
         lib.oracle_dense_split_partials.restype = I
         lib.oracle_combine.argtypes = [I, I, I, P, P, P, P]
         lib.oracle_combine.restype = None
@@ -126,8 +128,10 @@ def decode16(bits, dtype):
 
 
 def paged_attention(q, k_cache, v_cache, block_table, cache_seqlens, dtype, scale=None,
-                    nthreads=None):
+                    nthreads=None, causal=False):
     """Exact attention over a paged KV cache (two-pass softmax, float64).
+
+    causal: query i of qlen sees keys j <= L - qlen + i (bottom-right).
 
     q: uint16 [B, qlen, Hq, d]; k_cache, v_cache: uint16 [pages, page, Hkv, d];
     block_table: int32 [B, max_pages]; cache_seqlens: int32 [B].
@@ -145,14 +149,14 @@ def paged_attention(q, k_cache, v_cache, block_table, cache_seqlens, dtype, scal
     out = np.zeros((B, qlen, hq, d), dtype=np.float64)
     lse = np.zeros((B, hq, qlen), dtype=np.float64)
     rc = lib.oracle_paged_attention(B, qlen, hq, hkv, d, page, bt.shape[1], _dt(dtype), _p(q),
-                                    _p(kc), _p(vc), _p(bt), _p(sl), float(scale),
+                                    _p(kc), _p(vc), _p(bt), _p(sl), float(scale), int(causal),
                                     nthreads or default_threads(), _p(out), _p(lse))
     if rc != 0:
         raise ValueError("oracle_paged_attention rejected the shape")
     return out, lse
 
 
-def dense_attention(q, k, v, dtype, scale=None, nthreads=None):
+def dense_attention(q, k, v, dtype, scale=None, nthreads=None, causal=False):
     """Exact attention, dense K/V (two-pass softmax, float64).
 
     q: uint16 [Hq, qlen, d]; k, v: uint16 [Hkv, kvlen, d].
@@ -168,7 +172,8 @@ def dense_attention(q, k, v, dtype, scale=None, nthreads=None):
     out = np.zeros((hq, qlen, d), dtype=np.float64)
     lse = np.zeros((hq, qlen), dtype=np.float64)
     rc = lib.oracle_dense_attention(hq, hkv, qlen, kvlen, d, _dt(dtype), _p(q), _p(k), _p(v),
-                                    float(scale), nthreads or default_threads(), _p(out), _p(lse))
+                                    float(scale), int(causal), nthreads or default_threads(),
+                                    _p(out), _p(lse))
     if rc != 0:
         raise ValueError("oracle_dense_attention rejected the shape")
     return out, lse
@@ -182,7 +187,7 @@ def split_keys_for(max_len, num_splits, granule=16):
 
 
 def paged_split_partials(q, k_cache, v_cache, block_table, cache_seqlens, dtype, num_splits,
-                         split_keys, block=16, scale=None, nthreads=None):
+                         split_keys, block=16, scale=None, nthreads=None, causal=False):
     """Per-split partials via the online-softmax recurrence (float64).
 
     Split s of a sequence with L keys covers keys [s*C, (s+1)*C) clipped to
@@ -202,7 +207,7 @@ def paged_split_partials(q, k_cache, v_cache, block_table, cache_seqlens, dtype,
     l = np.zeros((num_splits, n), dtype=np.float64)
     rc = lib.oracle_paged_split_partials(B, qlen, hq, hkv, d, page, bt.shape[1], _dt(dtype),
                                          _p(q), _p(kc), _p(vc), _p(bt), _p(sl), float(scale),
-                                         num_splits, split_keys, block,
+                                         int(causal), num_splits, split_keys, block,
                                          nthreads or default_threads(), _p(o), _p(l))
     if rc != 0:
         raise ValueError("oracle_paged_split_partials rejected the shape")
@@ -210,7 +215,7 @@ def paged_split_partials(q, k_cache, v_cache, block_table, cache_seqlens, dtype,
 
 
 def dense_split_partials(q, k, v, dtype, num_splits, split_keys, block=16, scale=None,
-                         nthreads=None):
+                         nthreads=None, causal=False):
     """Dense-layout counterpart of paged_split_partials; rows n = hq*qlen + i."""
     lib = _load()
     q, k, v = _u16(q), _u16(k), _u16(v)
@@ -222,7 +227,7 @@ def dense_split_partials(q, k, v, dtype, num_splits, split_keys, block=16, scale
     o = np.zeros((num_splits, n, d), dtype=np.float64)
     l = np.zeros((num_splits, n), dtype=np.float64)
     rc = lib.oracle_dense_split_partials(hq, hkv, qlen, kvlen, d, _dt(dtype), _p(q), _p(k), _p(v),
-                                         float(scale), num_splits, split_keys, block,
+                                         float(scale), int(causal), num_splits, split_keys, block,
                                          nthreads or default_threads(), _p(o), _p(l))
     if rc != 0:
         raise ValueError("oracle_dense_split_partials rejected the shape")

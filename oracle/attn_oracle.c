@@ -40,6 +40,13 @@
  *   [s*C, (s+1)*C) clipped to [0, L), with one split length C for the whole
  *   batch (callers take C = 16*ceil(ceil(maxL/16)/S)); an empty split gives
  *   (O_s = 0, LSE_s = -inf); the combine is the max-shifted log-sum-exp merge.
+ *
+ *   Causal (the lpnh.cn article's flash_attn_with_kvcache(..., causal=True)
+ *   example in section "num_splits 怎么选"; the pages do not define the
+ *   alignment): the qlen new queries are the last qlen positions of the
+ *   sequence, so query i of qlen sees keys j <= L - qlen + i, i.e. the first
+ *   max(0, L - qlen + 1 + i) keys (bottom-right alignment).  A row that sees
+ *   no key is an empty row (O = 0, LSE = -inf).
  */
 #include <math.h>
 #include <pthread.h>
@@ -263,6 +270,15 @@ static void free_tables(tables_t *T, int nrows) {
     free(T->vpool);
 }
 
+/* Keys query i of qlen sees in a sequence of L keys. */
+static int visible_keys(int L, int qlen, int i, int causal) {
+    int n;
+    if (!causal) return L;
+    n = L - qlen + 1 + i;
+    if (n < 0) n = 0;
+    return n < L ? n : L;
+}
+
 /*
  * Paged layout.  q, out: [B, qlen, Hq, d]; lse: [B, Hq, qlen];
  * k_cache, v_cache: [num_pages, page_size, Hkv, d];
@@ -272,7 +288,7 @@ static void free_tables(tables_t *T, int nrows) {
  */
 static int build_paged(tables_t *T, int B, int qlen, int hq, int hkv, int d, int page_size,
                        int max_pages, const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
-                       const int32_t *bt, const int32_t *seqlens) {
+                       const int32_t *bt, const int32_t *seqlens, int causal) {
     int nrows = B * qlen * hq, G = hq / hkv;
     long total = 0;
     int b, i, h, j;
@@ -301,7 +317,7 @@ static int build_paged(tables_t *T, int B, int qlen, int hq, int hkv, int d, int
                     int hh = h * G + g;
                     int n = (b * qlen + i) * hq + hh;
                     T->qrow[n] = q + (size_t)n * d;
-                    T->len[n] = L;
+                    T->len[n] = visible_keys(L, qlen, i, causal);
                     T->krow[n] = kt;
                     T->vrow[n] = vt;
                 }
@@ -315,7 +331,7 @@ static int build_paged(tables_t *T, int B, int qlen, int hq, int hkv, int d, int
 /* Dense layout.  q, out: [Hq, qlen, d]; lse: [Hq, qlen]; k, v: [Hkv, kvlen, d].
  * Row n = hq * qlen + i. */
 static void build_dense(tables_t *T, int hq, int hkv, int qlen, int kvlen, int d,
-                        const uint16_t *q, const uint16_t *k, const uint16_t *v) {
+                        const uint16_t *q, const uint16_t *k, const uint16_t *v, int causal) {
     int nrows = hq * qlen, G = hq / hkv;
     int h, i, j, hh;
     T->qrow = (const uint16_t **)malloc(sizeof(void *) * (size_t)(nrows > 0 ? nrows : 1));
@@ -334,7 +350,7 @@ static void build_dense(tables_t *T, int hq, int hkv, int qlen, int kvlen, int d
             int n = hh * qlen + i;
             h = hh / G;
             T->qrow[n] = q + (size_t)n * d;
-            T->len[n] = kvlen;
+            T->len[n] = visible_keys(kvlen, qlen, i, causal);
             T->krow[n] = T->kpool + (long)h * kvlen;
             T->vrow[n] = T->vpool + (long)h * kvlen;
         }
@@ -350,14 +366,15 @@ static int check_common(int hq, int hkv, int d) {
 int oracle_paged_attention(int B, int qlen, int hq, int hkv, int d, int page_size, int max_pages,
                            int dtype, const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
                            const int32_t *block_table, const int32_t *seqlens, double scale,
-                           int nthreads, double *out, double *lse) {
+                           int causal, int nthreads, double *out, double *lse) {
     tables_t T;
     problem_t P;
     int nrows = B * qlen * hq, b, i, h;
     double *lse_rows;
     if (check_common(hq, hkv, d) || page_size <= 0) return -1;
     memset(&T, 0, sizeof(T));
-    if (build_paged(&T, B, qlen, hq, hkv, d, page_size, max_pages, q, kc, vc, block_table, seqlens)) {
+    if (build_paged(&T, B, qlen, hq, hkv, d, page_size, max_pages, q, kc, vc, block_table, seqlens,
+                    causal)) {
         free_tables(&T, nrows);
         return -1;
     }
@@ -381,12 +398,12 @@ int oracle_paged_attention(int B, int qlen, int hq, int hkv, int d, int page_siz
 /* Exact attention, dense K/V.  out [Hq,qlen,d], lse [Hq,qlen]. */
 int oracle_dense_attention(int hq, int hkv, int qlen, int kvlen, int d, int dtype,
                            const uint16_t *q, const uint16_t *k, const uint16_t *v, double scale,
-                           int nthreads, double *out, double *lse) {
+                           int causal, int nthreads, double *out, double *lse) {
     tables_t T;
     problem_t P;
     if (check_common(hq, hkv, d) || kvlen < 0) return -1;
     memset(&T, 0, sizeof(T));
-    build_dense(&T, hq, hkv, qlen, kvlen, d, q, k, v);
+    build_dense(&T, hq, hkv, qlen, kvlen, d, q, k, v, causal);
     memset(&P, 0, sizeof(P));
     P.nrows = hq * qlen; P.d = d; P.dtype = dtype; P.scale = scale;
     P.qrow = T.qrow; P.len = T.len;
@@ -405,8 +422,9 @@ int oracle_dense_attention(int hq, int hkv, int qlen, int kvlen, int d, int dtyp
 int oracle_paged_split_partials(int B, int qlen, int hq, int hkv, int d, int page_size,
                                 int max_pages, int dtype, const uint16_t *q, const uint16_t *kc,
                                 const uint16_t *vc, const int32_t *block_table,
-                                const int32_t *seqlens, double scale, int num_splits, int split_keys,
-                                int block, int nthreads, double *o_part, double *lse_part) {
+                                const int32_t *seqlens, double scale, int causal, int num_splits,
+                                int split_keys, int block, int nthreads, double *o_part,
+                                double *lse_part) {
     tables_t T;
     problem_t P;
     int nrows = B * qlen * hq;
@@ -415,7 +433,8 @@ int oracle_paged_split_partials(int B, int qlen, int hq, int hkv, int d, int pag
     for (b = 0; b < B; ++b) /* the splits must cover every key */
         if ((long)num_splits * split_keys < seqlens[b]) return -1;
     memset(&T, 0, sizeof(T));
-    if (build_paged(&T, B, qlen, hq, hkv, d, page_size, max_pages, q, kc, vc, block_table, seqlens)) {
+    if (build_paged(&T, B, qlen, hq, hkv, d, page_size, max_pages, q, kc, vc, block_table, seqlens,
+                    causal)) {
         free_tables(&T, nrows);
         return -1;
     }
@@ -434,14 +453,14 @@ int oracle_paged_split_partials(int B, int qlen, int hq, int hkv, int d, int pag
 /* Split partials, dense layout.  Rows n = hq*qlen+i. */
 int oracle_dense_split_partials(int hq, int hkv, int qlen, int kvlen, int d, int dtype,
                                 const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                double scale, int num_splits, int split_keys, int block,
-                                int nthreads, double *o_part, double *lse_part) {
+                                double scale, int causal, int num_splits, int split_keys,
+                                int block, int nthreads, double *o_part, double *lse_part) {
     tables_t T;
     problem_t P;
     if (check_common(hq, hkv, d) || kvlen < 0 || num_splits < 1 || split_keys < 1) return -1;
     if ((long)num_splits * split_keys < kvlen) return -1; /* the splits must cover every key */
     memset(&T, 0, sizeof(T));
-    build_dense(&T, hq, hkv, qlen, kvlen, d, q, k, v);
+    build_dense(&T, hq, hkv, qlen, kvlen, d, q, k, v, causal);
     memset(&P, 0, sizeof(P));
     P.nrows = hq * qlen; P.d = d; P.dtype = dtype; P.scale = scale;
     P.qrow = T.qrow; P.len = T.len;

@@ -37,6 +37,8 @@ MUTATIONS = [
     ("fp16 subnormal scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     ("bf16 exponent bias", "v = ldexp((double)(128 + f), e - 134);",
      "v = ldexp((double)(128 + f), e - 133);"),
+    ("causal off by one", "n = L - qlen + 1 + i;", "n = L - qlen + i;"),
+    ("causal top-left aligned", "n = L - qlen + 1 + i;", "n = 1 + i;"),
     ("empty sequence lse", "if (j1 <= j0) {\n        *lse = -INFINITY;\n        return;\n    }\n    s =",
      "if (j1 <= j0) {\n        *lse = 0.0;\n        return;\n    }\n    s ="),
 ]
@@ -56,6 +58,9 @@ PIN_TESTS = [
     (pins.test_split_partials_and_combine_equal_direct, dict(block=5)),
     (pins.test_split_ranges_cover_keys_once_and_empty_splits_are_neutral, {}),
     (pins.test_combine_closed_forms, {}),
+    (pins.test_causal_dense_matches_torch_with_bottom_right_mask,
+     dict(hq=8, hkv=2, qlen=4, L=33, d=64)),
+    (pins.test_causal_closed_forms, {}),
 ]
 
 

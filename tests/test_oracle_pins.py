@@ -173,6 +173,115 @@ def test_paged_matches_torch_sdpa_on_gathered_kv(dtype, G, d, page):
         np.testing.assert_allclose(lse[b], rl, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ causal --
+# Bottom-right alignment: the q_len queries are the last q_len positions, so
+# query i sees keys j <= L - q_len + i.  The mask below is built from that
+# sentence alone and handed to torch's attention in float64.
+
+def _causal_mask(qlen, L):
+    i = np.arange(qlen)[:, None]
+    j = np.arange(L)[None, :]
+    return j <= L - qlen + i
+
+
+def _sdpa_masked(qb, kb, vb, scale, mask):
+    """torch float64 attention with a boolean [n, L] mask; rows that see no
+    key come back as None."""
+    G = qb.shape[0] // kb.shape[0]
+    q = torch.from_numpy(qb)
+    k = torch.from_numpy(kb).repeat_interleave(G, dim=0)
+    v = torch.from_numpy(vb).repeat_interleave(G, dim=0)
+    m = torch.from_numpy(mask)
+    live = mask.any(axis=1)
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=scale)
+    s = (torch.matmul(q, k.transpose(-1, -2)) * scale).numpy()
+    s = np.where(mask[None], s, -np.inf)
+    lse = np.full(s.shape[:2], -np.inf)
+    lse[:, live] = scipy.special.logsumexp(s[:, live], axis=-1)
+    return out.numpy(), lse, live
+
+
+@pytest.mark.parametrize("hq,hkv,qlen,L,d", [(4, 2, 3, 9, 8), (8, 2, 4, 33, 64), (8, 8, 8, 8, 16),
+                                             (4, 1, 6, 3, 24), (2, 2, 5, 70, 128)])
+def test_causal_dense_matches_torch_with_bottom_right_mask(hq, hkv, qlen, L, d):
+    wl = W.make_dense(31 + L + qlen, "bf16", hq, hkv, qlen, L, d)
+    out, lse = oracle.dense_attention(wl.q, wl.k, wl.v, "bf16", causal=True)
+    mask = _causal_mask(qlen, L)
+    ro, rl, live = _sdpa_masked(f64(wl.q, "bf16"), f64(wl.k, "bf16"), f64(wl.v, "bf16"),
+                                1.0 / math.sqrt(d), mask)
+    np.testing.assert_allclose(out[:, live], ro[:, live], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[:, live], rl[:, live], rtol=1e-12, atol=1e-12)
+    assert np.all(out[:, ~live] == 0) and np.all(np.isneginf(lse[:, ~live]))
+
+
+@pytest.mark.parametrize("G,qlen,page", [(4, 4, 16), (1, 8, 16), (2, 3, 5)])
+def test_causal_paged_matches_torch_on_gathered_kv(G, qlen, page):
+    hkv, B, d = 2, 3, 32
+    lens = [2, qlen, 2 * page + 3]  # first one shorter than q_len: an empty row
+    wl = W.make_paged(41 + G + qlen, "fp16", B, qlen, G * hkv, hkv, d, page, lens, spare_pages=2)
+    out, lse = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                      wl.cache_seqlens, "fp16", causal=True)
+    kc, vc = f64(wl.k_cache, "fp16"), f64(wl.v_cache, "fp16")
+    qf = f64(wl.q, "fp16")
+    for b in range(B):
+        L = lens[b]
+        pages = wl.block_table[b, :(L + page - 1) // page]
+        kseq = kc[pages].reshape(-1, hkv, d)[:L].transpose(1, 0, 2).copy()
+        vseq = vc[pages].reshape(-1, hkv, d)[:L].transpose(1, 0, 2).copy()
+        ro, rl, live = _sdpa_masked(qf[b].transpose(1, 0, 2).copy(), kseq, vseq,
+                                    1.0 / math.sqrt(d), _causal_mask(qlen, L))
+        ob = out[b].transpose(1, 0, 2)  # [Hq, qlen, d]
+        np.testing.assert_allclose(ob[:, live], ro[:, live], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b][:, live], rl[:, live], rtol=1e-12, atol=1e-12)
+        assert np.all(ob[:, ~live] == 0) and np.all(np.isneginf(lse[b][:, ~live]))
+
+
+def test_causal_closed_forms():
+    """q_len = L: query 0 sees key 0 only (O = v_0 exactly, LSE = s_00);
+    query 1 sees keys 0 and 1 (logistic weights); the last query sees all."""
+    rng = np.random.default_rng(5)
+    L = 4
+    q = rng.standard_normal((1, L, 8)).astype(np.float32)
+    k = rng.standard_normal((1, L, 8)).astype(np.float32)
+    v = rng.standard_normal((1, L, 8)).astype(np.float32)
+    qb, kb, vb = (W.to_bits(x, "fp16") for x in (q, k, v))
+    out, lse = oracle.dense_attention(qb, kb, vb, "fp16", scale=0.5, causal=True)
+    qf, kf, vf = f64(qb, "fp16")[0], f64(kb, "fp16")[0], f64(vb, "fp16")[0]
+    s = 0.5 * qf @ kf.T
+    assert np.array_equal(out[0, 0], vf[0])
+    assert lse[0, 0] == s[0, 0]
+    w1 = 1.0 / (1.0 + math.exp(s[1, 1] - s[1, 0]))
+    np.testing.assert_allclose(out[0, 1], w1 * vf[0] + (1 - w1) * vf[1], rtol=1e-13, atol=1e-14)
+    full, full_lse = oracle.dense_attention(qb, kb, vb, "fp16", scale=0.5)
+    assert np.array_equal(out[0, L - 1], full[0, L - 1]) and lse[0, L - 1] == full_lse[0, L - 1]
+
+
+def test_causal_with_one_query_changes_nothing():
+    wl = W.make_paged(51, "bf16", 3, 1, 8, 2, 64, 16, [1, 17, 100], spare_pages=1)
+    a = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.cache_seqlens,
+                               "bf16")
+    b = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.cache_seqlens,
+                               "bf16", causal=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_causal_split_partials_combine_to_direct():
+    wl = W.make_paged(61, "bf16", 2, 5, 8, 2, 64, 16, [3, 77], spare_pages=1)
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, "bf16", causal=True)
+    for S in (1, 2, 3, 6):
+        C = oracle.split_keys_for(77, S)
+        o, l = oracle.paged_split_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                           wl.cache_seqlens, "bf16", S, C, block=16, causal=True)
+        out, lse = oracle.combine(o, l)
+        n = 2 * 5 * 8
+        np.testing.assert_allclose(out, ref_o.reshape(n, 64), rtol=1e-12, atol=1e-12)
+        ref = ref_l.transpose(0, 2, 1).reshape(n)
+        live = ~np.isneginf(ref)
+        np.testing.assert_allclose(lse[live], ref[live], rtol=1e-12, atol=1e-12)
+        assert np.array_equal(np.isneginf(lse), ~live)
+
+
 # --------------------------------------------------------------- invariants --
 
 def test_value_and_lse_bounds():
