@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
     ATTN_OK = 0,
@@ -162,6 +162,32 @@ attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const
                             const int32_t* cache_seqlens, int num_splits, int pack_gqa,
                             float softmax_scale, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Paged decode forward with the options of the flash_attn_with_kvcache call
+ * in the lpnh.cn article (section "num_splits 怎么选"): keys appended to the
+ * cache in the same call, and a causal mask for q_len > 1 (speculative /
+ * MTP verification).  Other arguments as in attn_decode_fwd, which is this
+ * call with new_len = 0 and causal = 0.
+ *   k_new, v_new  [batch, new_len, num_heads_kv, head_dim], 16-byte aligned;
+ *                 may be NULL when new_len == 0.
+ *   new_len       keys appended per sequence (>= 0).  They are written to
+ *                 key positions cache_seqlens[b] .. cache_seqlens[b] +
+ *                 new_len - 1 of k_cache / v_cache (the block table must map
+ *                 those pages), then attention covers L_b = cache_seqlens[b]
+ *                 + new_len keys.  cache_seqlens itself is not changed.
+ *                 shape->max_seqlen_k must bound every L_b.
+ *   causal        0: every query row sees all L_b keys.  1: query i of q_len
+ *                 sees keys j <= L_b - q_len + i (the queries are the last
+ *                 q_len positions: bottom-right alignment); a row that sees
+ *                 no key gets O = 0 and LSE = -inf.
+ * Errors: new_len < 0 or causal not 0/1 -> ATTN_ERR_ARG; new_len > 0 with a
+ * NULL k_new/v_new -> ATTN_ERR_NULL. */
+attn_status attn_decode_kvcache_fwd(const attn_decode_shape* shape, const void* q, void* k_cache,
+                                    void* v_cache, const int32_t* block_table,
+                                    const int32_t* cache_seqlens, const void* k_new,
+                                    const void* v_new, int new_len, int causal, int num_splits,
+                                    int pack_gqa, float softmax_scale, void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Plan a dense call (num_splits as above; always packed). */
 attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,

@@ -81,14 +81,17 @@ def _check_dev(*ts):
 
 def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pack_gqa=-1,
                softmax_scale=None, max_seqlen_k=None, out=None, lse=None, return_lse=True,
-               workspace=None, stream=None):
+               workspace=None, stream=None, k_new=None, v_new=None, causal=False):
     """Paged decode attention.
 
     q [B, q_len, Hq, d] fp16/bf16; k_cache, v_cache [pages, page, Hkv, d];
     block_table int32 [B, max_pages]; cache_seqlens int32 [B].
     Returns (out [B, q_len, Hq, d], lse float32 [B, Hq, q_len] or None).
-    max_seqlen_k (a host int bound on cache_seqlens) drives the plan; by
-    default it is max_pages * page_size, which needs no device sync.
+    max_seqlen_k (a host int bound on the attended lengths) drives the plan;
+    by default it is max_pages * page_size, which needs no device sync.
+    k_new / v_new [B, new_len, Hkv, d]: keys written into the cache at
+    positions cache_seqlens[b].. before attention (attn_decode_kvcache_fwd);
+    causal: query i of q_len sees keys j <= L - q_len + i.
     """
     _need(q.dtype in _DT and k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
           "q, k_cache, v_cache must share fp16 or bf16")
@@ -111,12 +114,30 @@ def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pa
             # zero-filled: the fused combine's arrival counters start at zero
             workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        code = lib.attn_decode_fwd(
-            ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-            _ptr(cache_seqlens), num_splits, pack_gqa,
-            float(softmax_scale) if softmax_scale else 0.0, _ptr(out), _ptr(lse),
-            _ptr(workspace), ws_bytes, _stream(dev, stream))
-    _L.check("attn_decode_fwd", code)
+        if k_new is None and not causal:
+            name = "attn_decode_fwd"
+            code = lib.attn_decode_fwd(
+                ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                _ptr(cache_seqlens), num_splits, pack_gqa,
+                float(softmax_scale) if softmax_scale else 0.0, _ptr(out), _ptr(lse),
+                _ptr(workspace), ws_bytes, _stream(dev, stream))
+        else:
+            name = "attn_decode_kvcache_fwd"
+            new_len = 0
+            if k_new is not None:
+                _need(v_new is not None and k_new.shape == v_new.shape and k_new.dim() == 4
+                      and k_new.shape[0] == q.shape[0] and k_new.shape[2:] == k_cache.shape[2:]
+                      and k_new.dtype == q.dtype and v_new.dtype == q.dtype
+                      and k_new.is_contiguous() and v_new.is_contiguous()
+                      and k_new.device == dev and v_new.device == dev,
+                      "k_new / v_new must be contiguous [B, new_len, Hkv, d] of q's dtype")
+                new_len = int(k_new.shape[1])
+            code = lib.attn_decode_kvcache_fwd(
+                ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                _ptr(cache_seqlens), _ptr(k_new), _ptr(v_new), new_len, int(bool(causal)),
+                num_splits, pack_gqa, float(softmax_scale) if softmax_scale else 0.0, _ptr(out),
+                _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _L.check(name, code)
     return out, lse
 
 

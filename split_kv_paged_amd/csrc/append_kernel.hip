@@ -1,0 +1,44 @@
+// append_kernel.hip -- write new keys and values into the paged KV cache.
+//
+// The lpnh.cn "pack_gqa 与 num_splits" article's example call passes new
+// keys and values with the cache (section "num_splits 怎么选"); they take
+// key positions cache_seqlens[b] .. cache_seqlens[b] + new_len - 1 of each
+// sequence, in the pages the block table maps there (PA_BBND layout of the
+// MixedQuantSparseFlashMla article, section 参数说明), before attention
+// reads the cache.  One workgroup per (sequence, new key) copies the Hkv
+// rows of K and V; the data is small, so 16-bit element copies are enough.
+#include "internal.h"
+
+namespace skv {
+namespace {
+
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
+  const int b = blockIdx.x / p.new_len;
+  const int t = blockIdx.x % p.new_len;
+  const int pos = p.seqlens[b] + t;
+  const int slot_page = pos / p.page_size;
+  if (pos < 0 || slot_page >= p.max_pages) return;  // outside the table: nothing to write
+  const long page = p.block_table[(long)b * p.max_pages + slot_page];
+  const long dst = ((page * p.page_size + pos % p.page_size) * p.hkv) * p.head_dim;
+  const long src = ((long)b * p.new_len + t) * p.hkv * p.head_dim;
+  const int n = p.hkv * p.head_dim;
+  const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + src;
+  const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + src;
+  uint16_t* kc = static_cast<uint16_t*>(p.k_cache) + dst;
+  uint16_t* vc = static_cast<uint16_t*>(p.v_cache) + dst;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    kc[e] = kn[e];
+    vc[e] = vn[e];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+  const long grid = (long)p.batch * p.new_len;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3(unsigned(grid)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace skv

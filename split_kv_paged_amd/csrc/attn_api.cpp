@@ -214,37 +214,18 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   return ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int pack_gqa,
-                             int num_cus, attn_plan* plan) {
-  if (!plan) return ATTN_ERR_NULL;
-  attn_status st = check_decode_shape(shape);
-  if (st != ATTN_OK) return st;
-  return make_plan(shape->batch, shape->q_len, shape->num_heads_q, shape->num_heads_kv,
-                   shape->head_dim, shape->max_seqlen_k, num_splits, pack_gqa, num_cus, false,
-                   plan);
-}
-
-attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,
-                            attn_plan* plan) {
-  if (!plan) return ATTN_ERR_NULL;
-  attn_status st = check_dense_shape(shape);
-  if (st != ATTN_OK) return st;
-  return make_plan(1, shape->q_len, shape->num_heads_q, shape->num_heads_kv, shape->head_dim,
-                   shape->kv_len, num_splits, -1, num_cus, true, plan);
-}
-
-attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const void* k_cache,
-                            const void* v_cache, const int32_t* block_table,
-                            const int32_t* cache_seqlens, int num_splits, int pack_gqa,
-                            float softmax_scale, void* out, float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+// Paged forward shared by attn_decode_fwd and attn_decode_kvcache_fwd.
+attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k_cache,
+                          void* v_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                          const void* k_new, const void* v_new, int new_len, int causal,
+                          int num_splits, int pack_gqa, float softmax_scale, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   attn_status st = check_decode_shape(shape);
   if (st != ATTN_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out) return ATTN_ERR_NULL;
+  if (new_len < 0 || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
+  if (new_len > 0 && (!k_new || !v_new)) return ATTN_ERR_NULL;
+  if (new_len > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16))) return ATTN_ERR_ALIGN;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(cache_seqlens, 4) || (lse && !aligned(lse, 4)))
     return ATTN_ERR_ALIGN;
@@ -280,9 +261,71 @@ attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const
   p.n_sb = shape->q_len * shape->num_heads_q;
   p.n_si = shape->num_heads_q;
   p.n_sh = 1;
+  p.seq_add = new_len;
+  p.causal = causal;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(D));
   p.scale_log2 = scale * 1.4426950408889634074f;
+  if (new_len > 0) {  // the new keys go into the cache first, on the same stream
+    skv::AppendParams a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seqlens = cache_seqlens;
+    a.batch = shape->batch;
+    a.new_len = new_len;
+    a.hkv = shape->num_heads_kv;
+    a.head_dim = D;
+    a.page_size = shape->page_size;
+    a.max_pages = shape->max_pages_per_seq;
+    if (skv::launch_append(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+  }
   return run(plan, p, true, shape->dtype, D, out, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int pack_gqa,
+                             int num_cus, attn_plan* plan) {
+  if (!plan) return ATTN_ERR_NULL;
+  attn_status st = check_decode_shape(shape);
+  if (st != ATTN_OK) return st;
+  return make_plan(shape->batch, shape->q_len, shape->num_heads_q, shape->num_heads_kv,
+                   shape->head_dim, shape->max_seqlen_k, num_splits, pack_gqa, num_cus, false,
+                   plan);
+}
+
+attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,
+                            attn_plan* plan) {
+  if (!plan) return ATTN_ERR_NULL;
+  attn_status st = check_dense_shape(shape);
+  if (st != ATTN_OK) return st;
+  return make_plan(1, shape->q_len, shape->num_heads_q, shape->num_heads_kv, shape->head_dim,
+                   shape->kv_len, num_splits, -1, num_cus, true, plan);
+}
+
+attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* cache_seqlens, int num_splits, int pack_gqa,
+                            float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_common(shape, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                       block_table, cache_seqlens, nullptr, nullptr, 0, 0, num_splits, pack_gqa,
+                       softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_kvcache_fwd(const attn_decode_shape* shape, const void* q, void* k_cache,
+                                    void* v_cache, const int32_t* block_table,
+                                    const int32_t* cache_seqlens, const void* k_new,
+                                    const void* v_new, int new_len, int causal, int num_splits,
+                                    int pack_gqa, float softmax_scale, void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(shape, q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new,
+                       new_len, causal, num_splits, pack_gqa, softmax_scale, out, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 attn_status attn_dense_fwd(const attn_dense_shape* shape, const void* q, const void* k,

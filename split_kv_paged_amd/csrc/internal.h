@@ -38,7 +38,23 @@ struct SplitParams {
   int n_sb, n_si, n_sh;
   float scale_log2;    // softmax scale * log2(e)
   int by_length;       // paged: run sequences longest first (batch <= kMaxOrderBatch)
+  int seq_add;         // paged: keys attended = seqlens[b] + seq_add (appended keys)
+  int causal;          // query i of q_len sees keys j <= L - q_len + i
 };
+
+// Append new_len keys per sequence to the paged cache (before attention):
+// k_new/v_new [batch, new_len, Hkv, head_dim] go to key positions
+// seqlens[b] .. seqlens[b] + new_len - 1.
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  int batch, new_len, hkv, head_dim, page_size, max_pages;
+};
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
 constexpr int kMaxOrderBatch = 1024;
 

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       return 0;
     }
   };
-  const int L = PAGED ? p.seqlens[b] : p.kv_len;
+  const int L = PAGED ? p.seqlens[b] + p.seq_add : p.kv_len;
   // Splits of this sequence that hold keys.  Past the last key a split has
   // nothing to add (its LSE would be -inf, weight zero in the combine), so
   // its workgroup leaves at once; a sequence that fits in one split is
@@ -234,6 +234,16 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 
   // ---- Q^T as the B operand: lane l holds row l%16, chunks g*KB + kb -----
   const int rowq = rb * 16 + n16;  // packed row of this lane in S^T
+  // Keys this lane's row may see: [t0, lim).  Causal (bottom-right): query i
+  // of q_len sees keys j <= L - q_len + i.  Tiles below t_full need no mask
+  // in any row.
+  int lim = t1;
+  int t_full = t1;
+  if (p.causal) {
+    const int i_row = rowq / p.heads_per_unit;
+    lim = min(t1, max(0, L - p.q_len + 1 + i_row));
+    t_full = min(t1, max(0, L - p.q_len + 1));
+  }
   uint4 qb[KB];
   {
     bool real = rowq < p.rows;
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     for (int kb = 0; kb < KB; ++kb) s = M::qk(bf.k[kb], qb[kb], s);
     if constexpr (!FULL) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (tt + 4 * g + i < t1) ? s[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) s[i] = (tt + 4 * g + i < lim) ? s[i] : -INFINITY;
     }
     // row max over the tile, lazy reference update
     float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -386,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   };
   auto process = [&](const Buf& bf, int idx) {
     const int tt = t0 + (wave + idx * NW) * kTile;
-    if (tt + kTile <= t1)
+    if (tt + kTile <= t_full)
       process_tile(bf, tt, std::true_type{});
     else
       process_tile(bf, tt, std::false_type{});

@@ -166,6 +166,21 @@ def test_dense_plan(lib):
         assert L.STATUS[lib.attn_dense_plan(ctypes.byref(bad), 0, 0, ctypes.byref(plan))] == want
 
 
+def test_kvcache_forward_argument_errors(lib):
+    """The append / causal entry point rejects bad options before any launch."""
+    P = ctypes.c_void_p
+    a = P(4096)
+    good = L.DecodeShape(2, 4, 8, 2, 128, 16, 8, 100, 1)
+    call = lambda new_len, causal, kn=a, vn=a: L.STATUS[lib.attn_decode_kvcache_fwd(
+        ctypes.byref(good), a, a, a, a, a, kn, vn, new_len, causal, 0, -1, 0.0, a, None, None, 0,
+        None)]
+    assert call(-1, 0) == "ATTN_ERR_ARG"
+    assert call(0, 2) == "ATTN_ERR_ARG"
+    assert call(3, 0, kn=None) == "ATTN_ERR_NULL"
+    assert call(3, 1, vn=None) == "ATTN_ERR_NULL"
+    assert call(3, 0, kn=P(4098)) == "ATTN_ERR_ALIGN"
+
+
 def test_forward_validation_before_any_device_call(lib):
     """Argument errors return before the library touches HIP."""
     P = ctypes.c_void_p

@@ -173,6 +173,81 @@ def test_paged_any_head_dim(d):
         assert_paged(wl, num_splits=S, ref=ref)
 
 
+# ------------------------------------------- causal small-q and KV append ----
+
+CAUSAL = [
+    # dtype, B, qlen, Hq, Hkv, d, lens
+    ("bf16", 3, 4, 32, 8, 128, [2, 4, 300]),     # GQA 4: 16 rows; L < q_len; L = q_len
+    ("fp16", 2, 8, 16, 2, 64, [9, 129]),         # GQA 8: 64 rows -> 4 row blocks
+    ("bf16", 2, 2, 8, 8, 128, [1, 77]),          # MHA, one query sees nothing in b 0
+    ("fp16", 2, 3, 8, 4, 96, [40, 1000]),        # any head dim
+    ("bf16", 2, 5, 8, 1, 64, [17, 18]),          # MQA, 40 rows
+]
+
+
+@pytest.mark.parametrize("spec", CAUSAL, ids=lambda s: "%s-q%d-%dx%d-d%d" % (s[0], s[2], s[3],
+                                                                            s[4], s[5]))
+@pytest.mark.parametrize("S", [0, 1, 3])
+def test_causal_paged(spec, S):
+    dt, B, qlen, hq, hkv, d, lens = spec
+    wl = W.make_paged(1200 + qlen * 10 + d, dt, B, qlen, hq, hkv, d, 16, lens, spare_pages=2,
+                      outlier_p=0.02)
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=True)
+    case("causal paged %s S=%d" % (str(spec), S))
+    q, kc, vc = to_dev(wl.q, dt), to_dev(wl.k_cache, dt), to_dev(wl.v_cache, dt)
+    out, lse = api.decode_fwd(q, kc, vc, i32_dev(wl.block_table), i32_dev(wl.cache_seqlens),
+                              num_splits=S, softmax_scale=wl.scale, max_seqlen_k=wl.max_seqlen_k,
+                              causal=True)
+    torch.cuda.synchronize()
+    e1 = check_out(bits_of(out), ref_o, dt)
+    e2 = check_lse(lse.cpu().numpy(), ref_l)
+    print("  S=%d max|dO|=%.3g max|dLSE|=%.3g" % (api.last_plan().num_splits, e1, e2), flush=True)
+
+
+def _append_case(seed, dt, B, qlen, hq, hkv, d, lens, new_len):
+    """A workload whose cache already holds L_b + new_len keys; the new rows
+    are cut out as k_new/v_new and poisoned in the cache the GPU sees."""
+    full = [L + new_len for L in lens]
+    wl = W.make_paged(seed, dt, B, qlen, hq, hkv, d, 16, full, spare_pages=2)
+    page = wl.page_size
+    k_new = np.zeros((B, new_len, hkv, d), dtype=np.uint16)
+    v_new = np.zeros_like(k_new)
+    kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
+    nan = {"fp16": 0x7E00, "bf16": 0x7FC0}[dt]
+    for b in range(B):
+        for t in range(new_len):
+            pos = lens[b] + t
+            pg, sl = wl.block_table[b, pos // page], pos % page
+            k_new[b, t], v_new[b, t] = wl.k_cache[pg, sl], wl.v_cache[pg, sl]
+            kc[pg, sl] = nan
+            vc[pg, sl] = nan
+    return wl, k_new, v_new, kc, vc
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [0, 4])
+def test_kv_append_then_attend(causal, S):
+    dt, B, qlen, hq, hkv, d, new_len = "bf16", 4, 4, 32, 8, 128, 4
+    lens = [0, 13, 500, 1020]
+    wl, k_new, v_new, kc_h, vc_h = _append_case(1300 + S, dt, B, qlen, hq, hkv, d, lens, new_len)
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    case("append %d keys then attend, causal=%s S=%d" % (new_len, causal, S))
+    kc, vc = to_dev(kc_h, dt), to_dev(vc_h, dt)
+    old = i32_dev(np.array(lens, dtype=np.int32))
+    out, lse = api.decode_fwd(to_dev(wl.q, dt), kc, vc, i32_dev(wl.block_table), old,
+                              num_splits=S, softmax_scale=wl.scale,
+                              max_seqlen_k=max(lens) + new_len, k_new=to_dev(k_new, dt),
+                              v_new=to_dev(v_new, dt), causal=causal)
+    torch.cuda.synchronize()
+    check_out(bits_of(out), ref_o, dt)
+    check_lse(lse.cpu().numpy(), ref_l)
+    # the cache now holds the full workload's bytes, and nothing else changed
+    assert np.array_equal(bits_of(kc), wl.k_cache) and np.array_equal(bits_of(vc), wl.v_cache)
+    assert np.array_equal(old.cpu().numpy(), np.array(lens, dtype=np.int32))
+
+
 # ------------------------------------------------------------- small shapes --
 
 SMALL = [
