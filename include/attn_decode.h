@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
     ATTN_OK = 0,
@@ -188,6 +188,30 @@ attn_status attn_decode_kvcache_fwd(const attn_decode_shape* shape, const void* 
                                     const void* v_new, int new_len, int causal, int num_splits,
                                     int pack_gqa, float softmax_scale, void* out, float* lse,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged decode forward with a different query count per sequence (varlen
+ * Q, the cu_seqlens input of the lpnh.cn article's section "pack_gqa 怎么选",
+ * which always packs the query heads of a KV head).
+ *   q, out        [total_q, num_heads_q, head_dim]: the queries of sequence b
+ *                 are rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1
+ *   cu_seqlens_q  int32 [batch + 1], cu_seqlens_q[0] = 0, non-decreasing,
+ *                 cu_seqlens_q[batch] = total_q, every difference <=
+ *                 shape->q_len (shape->q_len is the largest query count)
+ *   lse           float32 [num_heads_q, total_q], may be NULL
+ *   causal        as in attn_decode_kvcache_fwd, with each sequence's own
+ *                 query count
+ * Other arguments as in attn_decode_kvcache_fwd; pack_gqa is always on, so
+ * the plan (and workspace size) is attn_decode_plan's with pack_gqa = 1.
+ * Errors: total_q > batch * q_len -> ATTN_ERR_SHAPE; cu_seqlens_q NULL ->
+ * ATTN_ERR_NULL.  cu_seqlens_q's values are the caller's contract, like
+ * cache_seqlens. */
+attn_status attn_decode_varlen_fwd(const attn_decode_shape* shape, const void* q, void* k_cache,
+                                   void* v_cache, const int32_t* block_table,
+                                   const int32_t* cache_seqlens, const int32_t* cu_seqlens_q,
+                                   int total_q, const void* k_new, const void* v_new, int new_len,
+                                   int causal, int num_splits, float softmax_scale, void* out,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Plan a dense call (num_splits as above; always packed). */
 attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,

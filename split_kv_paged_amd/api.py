@@ -141,6 +141,60 @@ def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pa
     return out, lse
 
 
+def decode_varlen_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
+                      max_seqlen_q, num_splits=0, softmax_scale=None, max_seqlen_k=None,
+                      out=None, lse=None, return_lse=True, workspace=None, stream=None,
+                      k_new=None, v_new=None, causal=False):
+    """Paged decode attention with a query count per sequence.
+
+    q [total_q, Hq, d]; cu_seqlens_q int32 [B + 1] on the device (queries of
+    sequence b are rows cu[b]..cu[b+1]-1, at most max_seqlen_q of them).
+    Returns (out [total_q, Hq, d], lse float32 [Hq, total_q] or None).
+    """
+    _need(q.dim() == 3 and q.dtype in _DT and k_cache.dtype == q.dtype
+          and v_cache.dtype == q.dtype, "q [total_q, Hq, d]; q, k_cache, v_cache share a dtype")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.numel() == block_table.shape[0] + 1,
+          "cu_seqlens_q must be int32 [B + 1]")
+    dev = _check_dev(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, out, lse,
+                     workspace)
+    total_q, hq, d = q.shape
+    B = block_table.shape[0]
+    pages, page, hkv, d2 = k_cache.shape
+    _need(d2 == d, "head_dim")
+    maxp = block_table.shape[1]
+    shape = _L.DecodeShape(B, int(max_seqlen_q), hq, hkv, d, page, maxp,
+                           int(max_seqlen_k if max_seqlen_k is not None else maxp * page),
+                           _DT[q.dtype])
+    lib = _L.load()
+    plan = _L.Plan()
+    new_len = 0
+    if k_new is not None:
+        _need(v_new is not None and k_new.shape == v_new.shape and k_new.dim() == 4
+              and k_new.shape[0] == B and k_new.shape[2:] == k_cache.shape[2:]
+              and k_new.dtype == q.dtype and v_new.dtype == q.dtype and k_new.is_contiguous()
+              and v_new.is_contiguous(), "k_new / v_new must be contiguous [B, new_len, Hkv, d]")
+        new_len = int(k_new.shape[1])
+    with torch.cuda.device(dev):
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        _L.check("attn_decode_plan", lib.attn_decode_plan(ctypes.byref(shape), num_splits, 1,
+                                                          cus, ctypes.byref(plan)))
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and return_lse:
+            lse = torch.empty((hq, total_q), dtype=torch.float32, device=dev)
+        if workspace is None and plan.workspace_bytes > 0:
+            workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        code = lib.attn_decode_varlen_fwd(
+            ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(cache_seqlens), _ptr(cu_seqlens_q), int(total_q), _ptr(k_new), _ptr(v_new),
+            new_len, int(bool(causal)), num_splits,
+            float(softmax_scale) if softmax_scale else 0.0, _ptr(out), _ptr(lse),
+            _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _L.check("attn_decode_varlen_fwd", code)
+    return out, lse
+
+
 def dense_fwd(q, k, v, num_splits=0, softmax_scale=None, out=None, lse=None, return_lse=True,
               workspace=None, stream=None):
     """Dense small-query attention: q [Hq, q_len, d], k/v [Hkv, kv_len, d].

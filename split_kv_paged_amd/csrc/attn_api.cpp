@@ -73,7 +73,8 @@ int kernel_id(int head_dim, bool paged) {
 
 // Shared planner.  `dense` always packs (the dense API has no pack switch).
 attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, int64_t max_seqlen_k,
-                      int num_splits, int pack_gqa, int num_cus, bool dense, attn_plan* out) {
+                      int num_splits, int pack_gqa, int num_cus, bool dense, attn_plan* out,
+                      bool varlen = false) {
   if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
   if (pack_gqa < -1 || pack_gqa > 1) return ATTN_ERR_ARG;
   if (num_cus < 0) return ATTN_ERR_ARG;
@@ -83,7 +84,7 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   if (dense)
     pack = true;
   else if (pack_gqa < 0)
-    pack = should_pack_gqa(false, q_len, group, kBlockM);
+    pack = should_pack_gqa(varlen, q_len, group, kBlockM);
   else
     pack = pack_gqa == 1;
   int splits = num_splits;
@@ -219,13 +220,21 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
                           void* v_cache, const int32_t* block_table, const int32_t* cache_seqlens,
                           const void* k_new, const void* v_new, int new_len, int causal,
                           int num_splits, int pack_gqa, float softmax_scale, void* out, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          const int32_t* cu_q = nullptr, int total_q = 0) {
   attn_status st = check_decode_shape(shape);
   if (st != ATTN_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out) return ATTN_ERR_NULL;
   if (new_len < 0 || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
   if (new_len > 0 && (!k_new || !v_new)) return ATTN_ERR_NULL;
   if (new_len > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16))) return ATTN_ERR_ALIGN;
+  if (cu_q) {  // varlen queries: packed, at most q_len (= max_seqlen_q) per sequence
+    if (!aligned(cu_q, 4)) return ATTN_ERR_ALIGN;
+    if (total_q < 0 || int64_t(total_q) > int64_t(shape->batch) * shape->q_len)
+      return ATTN_ERR_SHAPE;
+    if (pack_gqa == 0) return ATTN_ERR_ARG;
+    pack_gqa = 1;
+  }
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(cache_seqlens, 4) || (lse && !aligned(lse, 4)))
     return ATTN_ERR_ALIGN;
@@ -234,7 +243,8 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
   const int cus = device_cus();
   if (cus <= 0) return ATTN_ERR_HIP;
   st = make_plan(shape->batch, shape->q_len, shape->num_heads_q, shape->num_heads_kv,
-                 shape->head_dim, shape->max_seqlen_k, num_splits, pack_gqa, cus, false, &plan);
+                 shape->head_dim, shape->max_seqlen_k, num_splits, pack_gqa, cus, false, &plan,
+                 cu_q != nullptr);
   if (st != ATTN_OK) return st;
   if ((st = check_workspace(plan, workspace, workspace_bytes)) != ATTN_OK) return st;
   if (shape->batch == 0) {
@@ -258,11 +268,12 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
   p.max_pages = shape->max_pages_per_seq;
   p.kv_len = 0;
   p.nrows = shape->batch * shape->q_len * shape->num_heads_q;
-  p.n_sb = shape->q_len * shape->num_heads_q;
   p.n_si = shape->num_heads_q;
   p.n_sh = 1;
   p.seq_add = new_len;
   p.causal = causal;
+  p.cu_q = cu_q;
+  p.total_q = total_q;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(D));
   p.scale_log2 = scale * 1.4426950408889634074f;
   if (new_len > 0) {  // the new keys go into the cache first, on the same stream
@@ -317,6 +328,19 @@ attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const
                        softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+attn_status attn_decode_varlen_fwd(const attn_decode_shape* shape, const void* q, void* k_cache,
+                                   void* v_cache, const int32_t* block_table,
+                                   const int32_t* cache_seqlens, const int32_t* cu_seqlens_q,
+                                   int total_q, const void* k_new, const void* v_new, int new_len,
+                                   int causal, int num_splits, float softmax_scale, void* out,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!cu_seqlens_q) return ATTN_ERR_NULL;
+  return decode_common(shape, q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new,
+                       new_len, causal, num_splits, -1, softmax_scale, out, lse, workspace,
+                       workspace_bytes, stream, cu_seqlens_q, total_q);
+}
+
 attn_status attn_decode_kvcache_fwd(const attn_decode_shape* shape, const void* q, void* k_cache,
                                     void* v_cache, const int32_t* block_table,
                                     const int32_t* cache_seqlens, const void* k_new,
@@ -359,7 +383,6 @@ attn_status attn_dense_fwd(const attn_dense_shape* shape, const void* q, const v
   p.max_pages = 0;
   p.kv_len = shape->kv_len;
   p.nrows = shape->num_heads_q * shape->q_len;
-  p.n_sb = 0;
   p.n_si = 1;
   p.n_sh = shape->q_len;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(D));

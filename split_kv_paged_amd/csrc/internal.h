@@ -7,9 +7,10 @@
 namespace skv {
 
 // One split-kernel launch.  Rows: a "row" is one (b, i, hq) query vector.
-//   row index n(b, i, hq) = b * n_sb + i * n_si + hq * n_sh
-//   q / out element offset = n * head_dim          (both layouts)
-//   lse index              = (b * Hq + hq) * q_len + i
+//   first query of sequence b: qb = cu_q ? cu_q[b] : b * q_len
+//   row index n(b, i, hq) = (qb + i) * n_si + hq * n_sh
+//   q / out element offset = n * head_dim          (all layouts)
+//   lse index              = (b * Hq + hq) * q_len + i, varlen: hq * total_q + qb + i
 // KV addressing of key t, KV head h:
 //   paged: page = block_table[b * max_pages + t / page_size],
 //          elem = ((page * page_size + t % page_size) * Hkv + h) * head_dim
@@ -35,11 +36,13 @@ struct SplitParams {
   int heads_per_unit;  // group (packed) or 1
   int unit_heads;      // Hkv (packed) or Hq
   int nrows;           // batch * q_len * Hq
-  int n_sb, n_si, n_sh;
+  int n_si, n_sh;
   float scale_log2;    // softmax scale * log2(e)
   int by_length;       // paged: run sequences longest first (batch <= kMaxOrderBatch)
   int seq_add;         // paged: keys attended = seqlens[b] + seq_add (appended keys)
   int causal;          // query i of q_len sees keys j <= L - q_len + i
+  const int32_t* cu_q; // varlen: queries of sequence b are rows cu_q[b] .. cu_q[b+1]-1
+  int total_q;         // varlen: cu_q[batch]; lse is [Hq, total_q]
 };
 
 // Append new_len keys per sequence to the paged cache (before attention):

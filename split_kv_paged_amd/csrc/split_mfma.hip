@@ -219,6 +219,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       return 0;
     }
   };
+  // queries of this sequence: rows qbase .. qbase + qlen_b - 1 of q / out
+  int qbase = b * p.q_len, qlen_b = p.q_len;
+  if (p.cu_q) {
+    qbase = p.cu_q[b];
+    qlen_b = p.cu_q[b + 1] - qbase;
+  }
+  const int rows_b = p.cu_q ? qlen_b * p.heads_per_unit : p.rows;  // real packed rows
+  if (rb * 16 >= rows_b) return;  // a row block past this sequence's queries
   const int L = PAGED ? p.seqlens[b] + p.seq_add : p.kv_len;
   // Splits of this sequence that hold keys.  Past the last key a split has
   // nothing to add (its LSE would be -inf, weight zero in the combine), so
@@ -241,17 +249,23 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   int t_full = t1;
   if (p.causal) {
     const int i_row = rowq / p.heads_per_unit;
-    lim = min(t1, max(0, L - p.q_len + 1 + i_row));
-    t_full = min(t1, max(0, L - p.q_len + 1));
+    lim = min(t1, max(0, L - qlen_b + 1 + i_row));
+    t_full = min(t1, max(0, L - qlen_b + 1));
   }
+  auto row_of = [&](int i, int hq) -> long {
+    return (long)(qbase + i) * p.n_si + (long)hq * p.n_sh;
+  };
+  auto lse_of = [&](int i, int hq) -> long {
+    return p.cu_q ? (long)hq * p.total_q + qbase + i : ((long)b * p.hq + hq) * p.q_len + i;
+  };
   uint4 qb[KB];
   {
-    bool real = rowq < p.rows;
+    bool real = rowq < rows_b;
     long n = 0;
     if (real) {
       const int i = rowq / p.heads_per_unit;
       const int hq = hq0 + rowq % p.heads_per_unit;
-      n = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
+      n = row_of(i, hq);
     }
     if constexpr (GEN) {
       const uint16_t* qr = static_cast<const uint16_t*>(p.q) + n * hd;
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   __shared__ float s_l[NW][RMAX];    // sums of the rounded probabilities (normalise O)
   __shared__ float s_l32[NW][RMAX];  // float32 sums (LSE)
   l32 = across_rows<false>(l32);
-  const int rows_here = min(RMAX, p.rows - rb * 16);
+  const int rows_here = min(RMAX, rows_b - rb * 16);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * g + i;
@@ -479,10 +493,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     const float lse = (Mx == -INFINITY) ? -INFINITY : (Mx + log2f(den32)) * kLn2;
     const int i = pr / p.heads_per_unit;
     const int hq = hq0 + pr % p.heads_per_unit;
-    const long nrow = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
+    const long nrow = row_of(i, hq);
     if (direct) {
       static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(o);
-      if (d == 0 && p.lse) p.lse[((long)b * p.hq + hq) * p.q_len + i] = lse;
+      if (d == 0 && p.lse) p.lse[lse_of(i, hq)] = lse;
     } else {  // write-through stores: the merging workgroup may sit on another XCD
       publish(r_opart, uint32_t(((long)split * p.nrows + nrow) * hd + d) * 4u, o);
       if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, lse);
@@ -518,7 +532,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     const int pr = rb * 16 + r;
     const int i = pr / p.heads_per_unit;
     const int hq = hq0 + pr % p.heads_per_unit;
-    const long nrow = (long)b * p.n_sb + (long)i * p.n_si + (long)hq * p.n_sh;
+    const long nrow = row_of(i, hq);
     float mx = -INFINITY, wsum = 0.f, acc_o = 0.f;  // log2 units
     for (int sp0 = 0; sp0 < S; sp0 += kBatch) {
       float ls[kBatch], o[kBatch];
@@ -548,8 +562,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     }
     static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(mx == -INFINITY ? 0.f : acc_o / wsum);
     if (d == 0 && p.lse)
-      p.lse[((long)b * p.hq + hq) * p.q_len + i] =
-          mx == -INFINITY ? -INFINITY : (mx + log2f(wsum)) * kLn2;
+      p.lse[lse_of(i, hq)] = mx == -INFINITY ? -INFINITY : (mx + log2f(wsum)) * kLn2;
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -19,8 +19,8 @@ FP16, BF16 = 0, 1
 
 # every symbol the header declares
 EXPORTS = (
-    "attn_decode_plan", "attn_decode_fwd", "attn_decode_kvcache_fwd", "attn_dense_plan",
-    "attn_dense_fwd",
+    "attn_decode_plan", "attn_decode_fwd", "attn_decode_kvcache_fwd", "attn_decode_varlen_fwd",
+    "attn_dense_plan", "attn_dense_fwd",
     "attn_combine_fwd", "attn_check_paged_inputs", "attn_last_plan", "attn_status_str",
     "attn_abi_version",
 )
@@ -74,6 +74,7 @@ def load():
         "attn_decode_plan": ([sd, I, I, I, pl], I),
         "attn_decode_fwd": ([sd, P, P, P, P, P, I, I, F, P, P, P, Z, P], I),
         "attn_decode_kvcache_fwd": ([sd, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, Z, P], I),
+        "attn_decode_varlen_fwd": ([sd, P, P, P, P, P, P, I, P, P, I, I, I, F, P, P, P, Z, P], I),
         "attn_dense_plan": ([sn, I, I, pl], I),
         "attn_dense_fwd": ([sn, P, P, P, I, F, P, P, P, Z, P], I),
         "attn_combine_fwd": ([I, I, I, I, I, I, P, P, P, P, P], I),

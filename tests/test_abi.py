@@ -181,6 +181,19 @@ def test_kvcache_forward_argument_errors(lib):
     assert call(3, 0, kn=P(4098)) == "ATTN_ERR_ALIGN"
 
 
+def test_varlen_forward_argument_errors(lib):
+    P = ctypes.c_void_p
+    a = P(4096)
+    good = L.DecodeShape(2, 4, 8, 2, 128, 16, 8, 100, 1)
+    call = lambda cu, total: L.STATUS[lib.attn_decode_varlen_fwd(
+        ctypes.byref(good), a, a, a, a, a, cu, total, None, None, 0, 0, 0, 0.0, a, None, None, 0,
+        None)]
+    assert call(None, 3) == "ATTN_ERR_NULL"
+    assert call(a, 9) == "ATTN_ERR_SHAPE"   # more queries than batch * q_len
+    assert call(a, -1) == "ATTN_ERR_SHAPE"
+    assert call(P(4098), 3) == "ATTN_ERR_ALIGN"
+
+
 def test_forward_validation_before_any_device_call(lib):
     """Argument errors return before the library touches HIP."""
     P = ctypes.c_void_p

@@ -248,6 +248,42 @@ def test_kv_append_then_attend(causal, S):
     assert np.array_equal(old.cpu().numpy(), np.array(lens, dtype=np.int32))
 
 
+# ------------------------------------------------------------- varlen Q ----
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [0, 1, 3])
+def test_varlen_queries(causal, S):
+    """A query count per sequence (cu_seqlens_q), packed; each sequence's
+    expected rows come from the oracle run on that sequence alone."""
+    dt, hq, hkv, d = "bf16", 16, 4, 128
+    qlens = [1, 4, 0, 7, 2]
+    lens = [30, 300, 64, 9, 1000]
+    B, maxq = len(lens), max(qlens)
+    wl = W.make_paged(1400 + S, dt, B, maxq, hq, hkv, d, 16, lens, spare_pages=2)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    total = int(cu[-1])
+    q = np.concatenate([wl.q[b, :qlens[b]] for b in range(B)], axis=0)  # [total, Hq, d]
+    ref_o = np.zeros((total, hq, d))
+    ref_l = np.full((hq, total), -np.inf)
+    for b in range(B):
+        if qlens[b] == 0:
+            continue
+        o, l = oracle.paged_attention(wl.q[b:b + 1, :qlens[b]], wl.k_cache, wl.v_cache,
+                                      wl.block_table[b:b + 1], wl.cache_seqlens[b:b + 1], dt,
+                                      scale=wl.scale, causal=causal)
+        ref_o[cu[b]:cu[b + 1]] = o[0]
+        ref_l[:, cu[b]:cu[b + 1]] = l[0]
+    case("varlen q_lens %s, causal=%s S=%d" % (qlens, causal, S))
+    out, lse = api.decode_varlen_fwd(to_dev(q, dt), to_dev(wl.k_cache, dt), to_dev(wl.v_cache, dt),
+                                     i32_dev(wl.block_table), i32_dev(wl.cache_seqlens),
+                                     i32_dev(cu), maxq, num_splits=S, softmax_scale=wl.scale,
+                                     max_seqlen_k=wl.max_seqlen_k, causal=causal)
+    torch.cuda.synchronize()
+    check_out(bits_of(out), ref_o, dt)
+    check_lse(lse.cpu().numpy(), ref_l)
+    assert api.last_plan().pack_gqa == 1
+
+
 # ------------------------------------------------------------- small shapes --
 
 SMALL = [
