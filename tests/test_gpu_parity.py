@@ -248,6 +248,29 @@ def test_kv_append_then_attend(causal, S):
     assert np.array_equal(old.cpu().numpy(), np.array(lens, dtype=np.int32))
 
 
+# ---------------------------------------------------------- ragged splits ----
+
+@pytest.mark.parametrize("lens", [
+    [1, 2, 3],                          # every split past the first is empty
+    [8192, 1, 1, 1, 1, 1, 1, 1],        # one long sequence, the rest in one split
+    [0, 5000, 0, 17, 3000, 1, 2047],    # empty sequences, long and short mixed
+    list(range(1, 400, 7)),             # many short sequences, 57 of them
+])
+@pytest.mark.parametrize("S", [0, 3, 8])
+def test_ragged_lengths_with_splits(lens, S):
+    """Per-sequence split counts: splits past a sequence's last key skip,
+    sequences within one split write directly, the rest merge; the grid runs
+    longest first (split-major, and ranked by length when unsplit)."""
+    wl = W.make_paged(1500 + len(lens), "fp16", len(lens), 1, 16, 8, 64, 16, lens,
+                      spare_pages=2, outlier_p=0.01)
+    ref = oracle_paged(wl)
+    case("ragged fp16 GQA2 d64, S=%d, lengths %s..." % (S, lens[:8]))
+    assert_paged(wl, num_splits=S, ref=ref)
+    a, la, _ = run_paged(wl, num_splits=S)
+    b, lb, _ = run_paged(wl, num_splits=S)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
 # ------------------------------------------------------------- varlen Q ----
 
 @pytest.mark.parametrize("causal", [False, True])
