@@ -183,7 +183,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(wl.name, last.num_splits),
             "kernel_avg_us": round(kern_s * 1e6, 3),
-            "kernels_per_launch": 1 + last.combine,
+            "kernels_per_launch": 1,
         },
     }
     if cpu is not None:

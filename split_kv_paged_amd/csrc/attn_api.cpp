@@ -203,11 +203,9 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
     prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
     prm.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + o_bytes + l_bytes);
   }
-  // Unsplit paged calls whose grid needs more than one round run the
-  // sequences longest first.  (With splits the split-major order already
-  // puts the long sequences' work first, and ranking in every workgroup,
-  // empty ones included, costs more than it saves.)
-  prm.by_length = paged && S == 1 && prm.batch <= skv::kMaxOrderBatch && plan.grid > plan.num_cus;
+  // Paged calls whose grid needs more than one round run the first split's
+  // sequences longest first (ranked inside its workgroups).
+  prm.by_length = paged && prm.batch <= skv::kMaxOrderBatch && plan.grid > plan.num_cus;
   if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   g_last_plan = plan;

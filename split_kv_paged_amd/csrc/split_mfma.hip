@@ -179,9 +179,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // Workgroups run split-major from the last split down: the last splits
   // exist only for the longest sequences, so their work is dispatched first
   // and the short remainder fills in behind it.
-  // When the grid takes more than one round of workgroups, the sequences
-  // also run longest first within each split (a longest-processing-time
-  // order): every workgroup ranks the batch by length, ties by index.
+  // When the grid takes more than one round of workgroups, the first split
+  // (the one every sequence has) also runs its sequences longest first (a
+  // longest-processing-time order): each of its workgroups ranks the batch
+  // by length, ties by index.  The later splits, mostly empty, skip that.
   const int units = p.batch * p.unit_heads * p.row_blocks;
   const int split = p.num_splits - 1 - int(blockIdx.x) / units;
   int bid = int(blockIdx.x) % units;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   bid /= p.row_blocks;
   const int uh = bid % p.unit_heads;
   int b = bid / p.unit_heads;
-  if (PAGED && p.by_length) {
+  if (PAGED && p.by_length && split == 0) {
     __shared__ int s_len[kMaxOrderBatch];
     __shared__ int s_seq;
     for (int i = threadIdx.x; i < p.batch; i += NW * 64) s_len[i] = p.seqlens[i];
