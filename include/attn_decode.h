@@ -75,9 +75,9 @@ typedef enum { ATTN_FP16 = 0, ATTN_BF16 = 1 } attn_dtype;
  *   cache_seqlens int32 [batch], number of valid keys of each sequence
  *   lse           float32 [batch, num_heads_q, q_len]
  * Supported: head_dim 1..256; page_size a multiple of 16; q_len >= 1 (no
- * causal mask: every query row sees all L keys); any G = Hq / Hkv.  head_dim
- * 32, 64, 128 and 256 move K/V in 16-byte loads; any other value is padded
- * inside the kernel and its elements are loaded one by one (slower). */
+ * causal mask: every query row sees all L keys); any G = Hq / Hkv.  Head
+ * dims are padded inside the kernel to 32, 64, 128 or 256; multiples of 8
+ * move K/V in 16-byte loads, other head dims element by element (slower). */
 typedef struct {
     int32_t batch;
     int32_t q_len;
@@ -121,9 +121,10 @@ typedef struct {
     int32_t combine;         /* how S > 1 partials are merged: 0 none (S = 1), */
                              /* 2 inside the split kernel by the last split to */
                              /* finish (1, a separate launch, is not used)     */
-    int32_t kernel;          /* diagnostic: 10000 (16-byte loads) or 20000     */
-                             /* (element loads) + 1000 if paged + tile head    */
-                             /* dim (32, 64, 128 or 256)                       */
+    int32_t kernel;          /* diagnostic: 10000 (16-byte loads), 20000      */
+                             /* (16-byte loads, head_dim a multiple of 8 below */
+                             /* the tile's) or 30000 (element loads) + 1000 if */
+                             /* paged + tile head dim (32, 64, 128 or 256)     */
     int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
     int64_t workspace_bytes; /* bytes of workspace the forward call needs     */

@@ -63,12 +63,14 @@ int num_splits_rule(int64_t total_mblocks, int num_cus, int64_t num_n_blocks) {
   return 1;
 }
 
-// Diagnostic kernel id: 10000 (16-byte loads) or 20000 (element loads for
-// any other head_dim) + 1000 if paged + the tile head dim (32/64/128/256).
+// Diagnostic kernel id: 10000 (16-byte loads), 20000 (16-byte loads with a
+// column mask: head_dim a multiple of 8) or 30000 (element loads: any other
+// head_dim) + 1000 if paged + the tile head dim (32/64/128/256).
 int kernel_id(int head_dim, bool paged) {
-  const bool fast = head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
+  const bool exact = head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
+  const int loads = exact ? 10000 : head_dim % 8 == 0 ? 20000 : 30000;
   const int tile = head_dim <= 32 ? 32 : head_dim <= 64 ? 64 : head_dim <= 128 ? 128 : 256;
-  return (fast ? 10000 : 20000) + (paged ? 1000 : 0) + tile;
+  return loads + (paged ? 1000 : 0) + tile;
 }
 
 // Shared planner.  `dense` always packs (the dense API has no pack switch).

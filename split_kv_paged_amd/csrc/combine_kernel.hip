@@ -11,7 +11,7 @@
 //
 // One wave per row; each lane streams head_dim/64 columns of every partial
 // (coalesced fp32 loads), so the pass reads S*(head_dim+1)*4 bytes per row
-// once.  Any head_dim in [1, 512].
+// once, kBatch splits per round of loads.  Any head_dim in [1, 512].
 #include "internal.h"
 
 namespace skv {
@@ -32,12 +32,17 @@ __device__ __forceinline__ uint16_t round16<1>(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-template <int DT>
+// KD = columns per lane / 1 (head_dim <= 64 * KD).  The partials of kBatch
+// splits are loaded in one round of independent loads, then folded in.
+constexpr int kBatch = 8;
+
+template <int DT, int KD>
 __global__ __launch_bounds__(kWaves * 64) void combine_kernel(const CombineParams p) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (n >= p.nrows) return;
   const int S = p.num_splits;
+  const int D = p.head_dim;
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, p.lse_part[(long)s * p.nrows + n]);
 #pragma unroll
@@ -46,7 +51,6 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(const CombineParam
         float, __builtin_amdgcn_ds_bpermute((lane ^ x) << 2, __builtin_bit_cast(int, M)));
     M = fmaxf(M, o);
   }
-  const int D = p.head_dim;
   uint16_t* out = static_cast<uint16_t*>(p.out);
   if (M == -INFINITY) {
     for (int d = lane; d < D; d += 64) out[(long)n * D + d] = round16<DT>(0.f);
@@ -56,23 +60,31 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(const CombineParam
     }
     return;
   }
-  float acc[8];
+  float acc[KD];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  for (int k = 0; k < KD; ++k) acc[k] = 0.f;
   float wsum = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ls = p.lse_part[(long)s * p.nrows + n];
-    const float w = (ls == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
-    wsum += w;
-    const float* os = p.o_part + ((long)s * p.nrows + n) * D;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float ls[kBatch], ov[kBatch][KD];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int d = lane + 64 * k;
-      if (d < D) acc[k] = fmaf(w, os[d], acc[k]);
+    for (int j = 0; j < kBatch; ++j) {  // clamped indices: no branches between the loads
+      const long row = (long)min(s0 + j, S - 1) * p.nrows + n;
+      ls[j] = p.lse_part[row];
+#pragma unroll
+      for (int k = 0; k < KD; ++k) ov[j][k] = p.o_part[row * D + min(lane + 64 * k, D - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = (s0 + j >= S || ls[j] == -INFINITY)
+                          ? 0.f
+                          : __builtin_amdgcn_exp2f((ls[j] - M) * kLog2e);
+      wsum += w;
+#pragma unroll
+      for (int k = 0; k < KD; ++k) acc[k] = fmaf(w, ov[j][k], acc[k]);
     }
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < KD; ++k) {
     const int d = lane + 64 * k;
     if (d < D) out[(long)n * D + d] = round16<DT>(acc[k] / wsum);
   }
@@ -82,15 +94,28 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(const CombineParam
   }
 }
 
+template <int DT>
+void launch_kd(const CombineParams& p, int grid, hipStream_t s) {
+  const int kd = (p.head_dim + 63) / 64;
+  if (kd <= 1)
+    hipLaunchKernelGGL((combine_kernel<DT, 1>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+  else if (kd <= 2)
+    hipLaunchKernelGGL((combine_kernel<DT, 2>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+  else if (kd <= 4)
+    hipLaunchKernelGGL((combine_kernel<DT, 4>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((combine_kernel<DT, 8>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+}
+
 }  // namespace
 
 hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t s) {
   if (p.nrows <= 0) return hipSuccess;
   const int grid = (p.nrows + kWaves - 1) / kWaves;
   if (dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, s, p);
+    launch_kd<1>(p, grid, s);
   else
-    hipLaunchKernelGGL(combine_kernel<0>, dim3(grid), dim3(kWaves * 64), 0, s, p);
+    launch_kd<0>(p, grid, s);
   return hipGetLastError();
 }
 

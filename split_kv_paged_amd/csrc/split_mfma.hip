@@ -147,13 +147,15 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
 }
 
 // D is the head dimension the tiles are built for (32, 64, 128 or 256); the
-// real one, p.head_dim <= D, may be any value.  With GEN false every key row
-// is D elements of 16-byte aligned memory and moves in 16-byte loads; with GEN
-// true (any other head_dim, the dense path's tails) each element is loaded on
-// its own and columns past p.head_dim read as zero, so they add nothing to the
-// scores and produce output columns that are never stored (the SmallQ README,
-// section "任意 headDim 支持": pad inside, store only the real columns).
-template <int DT, int D, int NW, int NBUF, bool PAGED, bool GEN>
+// real one, p.head_dim <= D, may be any value.  Columns past p.head_dim read
+// as zero, so they add nothing to the scores and produce output columns that
+// are never stored (the SmallQ README, section "任意 headDim 支持": pad
+// inside, store only the real columns).  GEN selects how K, V and Q move:
+//   0  head_dim == D: 16-byte loads;
+//   1  head_dim a multiple of 8 (rows stay 16-byte aligned): 16-byte loads,
+//      a chunk past the head dim gets an offset past the buffer range;
+//   2  any other head_dim: 16-bit element loads.
+template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN>
 __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
   using M = Mf<DT>;
   constexpr int KB = D / 32;        // 16x16x32 products per tile (QK)
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       const int hq = hq0 + rowq % p.heads_per_unit;
       n = row_of(i, hq);
     }
-    if constexpr (GEN) {
+    if constexpr (GEN == 2) {
       const uint16_t* qr = static_cast<const uint16_t*>(p.q) + n * hd;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -283,9 +285,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
         qb[kb] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     } else {
-      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * D);
+      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qb[kb] = real ? qp[g * KB + kb] : make_uint4(0, 0, 0, 0);
+      for (int kb = 0; kb < KB; ++kb)
+        qb[kb] = (real && (GEN == 0 || (g * KB + kb) * 8 < hd)) ? qp[g * KB + kb]
+                                                              : make_uint4(0, 0, 0, 0);
     }
   }
 
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     const uint32_t bytes = uint32_t(min(kTile, t1 - tt) * row_stride * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0, bytes);
-    if constexpr (GEN) {
+    if constexpr (GEN == 2) {
       // element loads; a column past the head dim gets an offset past the
       // descriptor's range, which reads as zero
 #pragma unroll
@@ -352,8 +356,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        bf.k[kb] = load16(rk, voff + kb * 16);
-        bf.v[kb] = load16(rv, voff + kb * 16);
+        const int off = (GEN == 0 || (g * KB + kb) * 8 < hd) ? voff + kb * 16 : kPastEnd;
+        bf.k[kb] = load16(rk, off);
+        bf.v[kb] = load16(rv, off);
       }
     }
   };
@@ -573,10 +578,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 // at D = 256 the accumulators and tiles leave room for one tile in flight
 // and the merge buffer for 4 waves; element loads at D = 128 also keep one
 // tile in flight (two would spill).
-template <int DT, int D, bool PAGED, bool GEN>
+template <int DT, int D, bool PAGED, int GEN>
 hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
   constexpr int NW = D <= 128 ? 8 : 4;
-  constexpr int NBUF = (D > 128 || (GEN && D == 128)) ? 1 : 2;
+  constexpr int NBUF = (D > 128 || (GEN == 2 && D == 128)) ? 1 : 2;
   hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN>), dim3(grid), dim3(NW * 64),
                      0, s, p);
   return hipGetLastError();
@@ -585,20 +590,23 @@ hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
 template <int DT, bool PAGED>
 hipError_t launch_mfma_dt(const SplitParams& p, int grid, hipStream_t s) {
   const int d = p.head_dim;
-  const bool gen = !(d == 32 || d == 64 || d == 128 || d == 256);
-  if (gen) {
-    if (d <= 32) return launch_mfma_d<DT, 32, PAGED, true>(p, grid, s);
-    if (d <= 64) return launch_mfma_d<DT, 64, PAGED, true>(p, grid, s);
-    if (d <= 128) return launch_mfma_d<DT, 128, PAGED, true>(p, grid, s);
-    if (d <= 256) return launch_mfma_d<DT, 256, PAGED, true>(p, grid, s);
+  switch (d) {
+    case 32: return launch_mfma_d<DT, 32, PAGED, 0>(p, grid, s);
+    case 64: return launch_mfma_d<DT, 64, PAGED, 0>(p, grid, s);
+    case 128: return launch_mfma_d<DT, 128, PAGED, 0>(p, grid, s);
+    case 256: return launch_mfma_d<DT, 256, PAGED, 0>(p, grid, s);
+  }
+  if (d % 8 == 0) {  // rows stay 16-byte aligned
+    if (d <= 32) return launch_mfma_d<DT, 32, PAGED, 1>(p, grid, s);
+    if (d <= 64) return launch_mfma_d<DT, 64, PAGED, 1>(p, grid, s);
+    if (d <= 128) return launch_mfma_d<DT, 128, PAGED, 1>(p, grid, s);
+    if (d <= 256) return launch_mfma_d<DT, 256, PAGED, 1>(p, grid, s);
     return hipErrorInvalidValue;
   }
-  switch (d) {
-    case 32: return launch_mfma_d<DT, 32, PAGED, false>(p, grid, s);
-    case 64: return launch_mfma_d<DT, 64, PAGED, false>(p, grid, s);
-    case 128: return launch_mfma_d<DT, 128, PAGED, false>(p, grid, s);
-    case 256: return launch_mfma_d<DT, 256, PAGED, false>(p, grid, s);
-  }
+  if (d <= 32) return launch_mfma_d<DT, 32, PAGED, 2>(p, grid, s);
+  if (d <= 64) return launch_mfma_d<DT, 64, PAGED, 2>(p, grid, s);
+  if (d <= 128) return launch_mfma_d<DT, 128, PAGED, 2>(p, grid, s);
+  if (d <= 256) return launch_mfma_d<DT, 256, PAGED, 2>(p, grid, s);
   return hipErrorInvalidValue;
 }
 

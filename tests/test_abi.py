@@ -118,13 +118,13 @@ def test_plan_fields_are_consistent(lib):
 
 def test_plan_kernel_ids_name_the_tile_and_load_path(lib):
     for d, want in [(64, 11064), (128, 11128), (32, 11032), (256, 11256), (96, 21128),
-                    (1, 21032), (200, 21256), (33, 21064)]:
+                    (1, 31032), (200, 21256), (33, 31064), (16, 21032), (130, 31256)]:
         code, plan = _plan(lib, batch=2, q_len=1, hq=8, hkv=2, max_L=512, maxp=32, d=d)
         assert code == 0 and plan.kernel == want, (d, plan.kernel)
     shape = L.DenseShape(8, 2, 1, 512, 80, 0)
     plan = L.Plan()
     assert lib.attn_dense_plan(ctypes.byref(shape), 0, 0, ctypes.byref(plan)) == 0
-    assert plan.kernel == 20128
+    assert plan.kernel == 20128  # 80: a multiple of 8, 16-byte loads with a column mask
 
 
 @pytest.mark.parametrize("field,value,want", [
