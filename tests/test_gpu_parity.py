@@ -271,6 +271,18 @@ def test_ragged_lengths_with_splits(lens, S):
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+@pytest.mark.parametrize("B", [1024, 2048])
+def test_large_batches(B):
+    """The largest batch that is ranked by length (1024) and one past it."""
+    rng = np.random.default_rng(B)
+    lens = [int(x) for x in rng.integers(0, 80, B)]
+    wl = W.make_paged(1600 + B, "bf16", B, 1, 8, 2, 64, 16, lens, spare_pages=2)
+    ref = oracle_paged(wl)
+    for S in (0, 2):
+        case("large batch B=%d GQA4 d64 L<80, S=%d" % (B, S))
+        assert_paged(wl, num_splits=S, ref=ref)
+
+
 # ------------------------------------------------------------- varlen Q ----
 
 @pytest.mark.parametrize("causal", [False, True])
