@@ -285,7 +285,7 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0,
                  pack_gqa=-1, softmax_scale=None, max_seqlen_k=None, out=None, lse=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, causal=False):
         _need(q.dtype in _DT and k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
               "q, k_cache, v_cache must share fp16 or bf16")
         dev = _check_dev(q, k_cache, v_cache, block_table, cache_seqlens, out, lse, workspace)
@@ -303,12 +303,17 @@ class PreparedDecode:
             workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         self.workspace = workspace
         self._keep = (q, k_cache, v_cache, block_table, cache_seqlens)
-        self.args = [ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                     _ptr(block_table), _ptr(cache_seqlens), int(num_splits), int(pack_gqa),
-                     float(softmax_scale) if softmax_scale else 0.0, _ptr(self.out),
-                     _ptr(self.lse), _ptr(workspace),
-                     workspace.numel() if workspace is not None else 0, _stream(dev, stream)]
-        self.fn = self.lib.attn_decode_fwd
+        tail = [int(num_splits), int(pack_gqa), float(softmax_scale) if softmax_scale else 0.0,
+                _ptr(self.out), _ptr(self.lse), _ptr(workspace),
+                workspace.numel() if workspace is not None else 0, _stream(dev, stream)]
+        head = [ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                _ptr(block_table), _ptr(cache_seqlens)]
+        if causal:  # attn_decode_kvcache_fwd with no appended keys
+            self.args = head + [None, None, 0, 1] + tail
+            self.fn = self.lib.attn_decode_kvcache_fwd
+        else:
+            self.args = head + tail
+            self.fn = self.lib.attn_decode_fwd
 
     def __call__(self, k_cache=None, v_cache=None):
         a = self.args
@@ -318,7 +323,7 @@ class PreparedDecode:
             a[3] = ctypes.c_void_p(v_cache.data_ptr())
         code = self.fn(*a)
         if code:
-            _L.check("attn_decode_fwd", code)
+            _L.check(self.fn.__name__, code)
         return self.out, self.lse
 
 

@@ -185,11 +185,24 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // (the one every sequence has) also runs its sequences longest first (a
   // longest-processing-time order): each of its workgroups ranks the batch
   // by length, ties by index.  The later splits, mostly empty, skip that.
+  // Within a split, the row blocks of one (sequence, head unit) sit 8
+  // workgroups apart: workgroups are dealt to the 8 XCDs round-robin, so
+  // they land on the same XCD, close in time, and the second one to read
+  // a KV tile finds it in that XCD's L2.  Head units go in groups of 8:
+  // workgroup g*8*RB + rb*n + i runs head unit 8g + i, row block rb, where
+  // n = 8 except in the last, shorter group.
   const int units = p.batch * p.unit_heads * p.row_blocks;
   const int split = p.num_splits - 1 - int(blockIdx.x) / units;
-  int bid = int(blockIdx.x) % units;
-  const int rb = bid % p.row_blocks;
-  bid /= p.row_blocks;
+  int rb, bid;
+  {
+    const int pairs = p.batch * p.unit_heads;
+    const int id = int(blockIdx.x) % units;
+    const int grp = id / (8 * p.row_blocks);
+    const int rem = id - grp * 8 * p.row_blocks;
+    const int n = min(8, pairs - grp * 8);
+    rb = rem / n;
+    bid = grp * 8 + rem % n;
+  }
   const int uh = bid % p.unit_heads;
   int b = bid / p.unit_heads;
   if (PAGED && p.by_length && split == 0) {
