@@ -99,7 +99,11 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   if (splits > 1) pack = true;  // same article, section "常见坑点"
 
   const int64_t rows_per_unit = pack ? int64_t(q_len) * group : q_len;
-  const int rpb = kRowsPerBlock;
+  // more than 16 rows: two 16-row blocks per workgroup (the KV is read once
+  // for 32 rows), where that kernel exists (16-byte loads, head dim 64/128)
+  const int rpb = (rows_per_unit > kRowsPerBlock && (head_dim == 64 || head_dim == 128))
+                      ? 2 * kRowsPerBlock
+                      : kRowsPerBlock;
   const int64_t row_blocks = ceil_div(rows_per_unit, rpb);
   const int64_t unit_heads = pack ? hkv : hq;
   const int64_t units = batch * unit_heads * row_blocks;
@@ -193,6 +197,7 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   prm.split_keys = plan.split_keys;
   prm.rows = plan.rows_per_unit;
   prm.row_blocks = plan.row_blocks;
+  prm.nrb = plan.rows_per_block / kRowsPerBlock;
   prm.heads_per_unit = plan.pack_gqa ? prm.group : 1;
   prm.unit_heads = plan.pack_gqa ? prm.hkv : prm.hq;
   prm.head_dim = head_dim;

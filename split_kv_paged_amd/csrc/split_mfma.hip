@@ -155,7 +155,9 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
 //   1  head_dim a multiple of 8 (rows stay 16-byte aligned): 16-byte loads,
 //      a chunk past the head dim gets an offset past the buffer range;
 //   2  any other head_dim: 16-bit element loads.
-template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN>
+// NRB: 16-row blocks a workgroup carries (1, or 2 when a unit has more
+// than 16 packed rows, so its KV is read once for 32 rows).
+template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB>
 __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
   using M = Mf<DT>;
   constexpr int KB = D / 32;        // 16x16x32 products per tile (QK)
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // workgroups apart: workgroups are dealt to the 8 XCDs round-robin, so
   // they land on the same XCD, close in time, and the second one to read
   // a KV tile finds it in that XCD's L2.  Head units go in groups of 8:
-  // workgroup g*8*RB + rb*n + i runs head unit 8g + i, row block rb, where
-  // n = 8 except in the last, shorter group.
+  // workgroup g*8*row_blocks + rb*n + i runs head unit 8g + i, row block
+  // rb, where n = 8 except in the last, shorter group.
   const int units = p.batch * p.unit_heads * p.row_blocks;
   const int split = p.num_splits - 1 - int(blockIdx.x) / units;
   int rb, bid;
@@ -242,7 +244,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     qlen_b = p.cu_q[b + 1] - qbase;
   }
   const int rows_b = p.cu_q ? qlen_b * p.heads_per_unit : p.rows;  // real packed rows
-  if (rb * 16 >= rows_b) return;  // a row block past this sequence's queries
+  const int row0 = rb * 16 * NRB;  // first packed row of this workgroup
+  if (row0 >= rows_b) return;      // a row block past this sequence's queries
   const int L = PAGED ? p.seqlens[b] + p.seq_add : p.kv_len;
   // Splits of this sequence that hold keys.  Past the last key a split has
   // nothing to add (its LSE would be -inf, weight zero in the combine), so
@@ -256,16 +259,21 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   const int n_tiles = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
-  // ---- Q^T as the B operand: lane l holds row l%16, chunks g*KB + kb -----
-  const int rowq = rb * 16 + n16;  // packed row of this lane in S^T
-  // Keys this lane's row may see: [t0, lim).  Causal (bottom-right): query i
-  // of q_len sees keys j <= L - q_len + i.  Tiles below t_full need no mask
-  // in any row.
-  int lim = t1;
+  // ---- Q^T as the B operand: lane l holds row l%16 of each 16-row block,
+  // chunks g*KB + kb ------------------------------------------------------
+  // Keys a lane's row may see: [t0, lim[r]).  Causal (bottom-right): query
+  // i of q_len sees keys j <= L - q_len + i.  Tiles below t_full need no
+  // mask in any row.
+  int lim[NRB];
   int t_full = t1;
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) lim[r] = t1;
   if (p.causal) {
-    const int i_row = rowq / p.heads_per_unit;
-    lim = min(t1, max(0, L - qlen_b + 1 + i_row));
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      const int i_row = (row0 + 16 * r + n16) / p.heads_per_unit;
+      lim[r] = min(t1, max(0, L - qlen_b + 1 + i_row));
+    }
     t_full = min(t1, max(0, L - qlen_b + 1));
   }
   auto row_of = [&](int i, int hq) -> long {
@@ -274,8 +282,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   auto lse_of = [&](int i, int hq) -> long {
     return p.cu_q ? (long)hq * p.total_q + qbase + i : ((long)b * p.hq + hq) * p.q_len + i;
   };
-  uint4 qb[KB];
-  {
+  uint4 qb[NRB][KB];
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) {
+    const int rowq = row0 + 16 * r + n16;  // packed row of this lane in block r of S^T
     bool real = rowq < rows_b;
     long n = 0;
     if (real) {
@@ -295,22 +305,27 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
           const uint32_t hi = (real && c0 + 1 < hd) ? qr[c0 + 1] : 0u;
           w[e] = lo | (hi << 16);
         }
-        qb[kb] = make_uint4(w[0], w[1], w[2], w[3]);
+        qb[r][kb] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     } else {
       const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        qb[kb] = (real && (GEN == 0 || (g * KB + kb) * 8 < hd)) ? qp[g * KB + kb]
-                                                              : make_uint4(0, 0, 0, 0);
+        qb[r][kb] = (real && (GEN == 0 || (g * KB + kb) * 8 < hd)) ? qp[g * KB + kb]
+                                                                 : make_uint4(0, 0, 0, 0);
     }
   }
 
-  f4_t acc[DB + 1];  // O blocks; acc[DB] is the all-ones block: column sums = l
+  f4_t acc[NRB][DB + 1];  // O blocks; acc[r][DB] is the all-ones block: column sums = l
+  float m[NRB];           // reference max of row n16 of block r (S^T layout), log2 units
+  float l32[NRB];         // float32 sum of this lane's probabilities (row n16)
 #pragma unroll
-  for (int db = 0; db <= DB; ++db) acc[db] = (f4_t){0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // reference max of row n16 (S^T layout), log2 units
-  float l32 = 0.f;      // float32 sum of this lane's probabilities (row n16)
+  for (int r = 0; r < NRB; ++r) {
+#pragma unroll
+    for (int db = 0; db <= DB; ++db) acc[r][db] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    m[r] = -INFINITY;
+    l32[r] = 0.f;
+  }
 
   const long row_stride = PAGED ? (long)p.hkv * hd : (long)hd;
   const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.k);
@@ -386,46 +401,58 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
         *reinterpret_cast<uint4*>(my_v + n16 * ROWB + (((g * KB + kb) ^ f_wr) * 16)) = bf.v[kb];
       else
         *reinterpret_cast<uint4*>(my_v + v_wr + kb * 16) = bf.v[kb];
-    // S^T = K . Q^T
-    f4_t s = {0.f, 0.f, 0.f, 0.f};
+    // S^T = K . Q^T for each row block (one K tile, NRB query blocks)
+    f4_t s[NRB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s = M::qk(bf.k[kb], qb[kb], s);
-    if constexpr (!FULL) {
+    for (int r = 0; r < NRB; ++r) {
+      s[r] = (f4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (tt + 4 * g + i < lim) ? s[i] : -INFINITY;
-    }
-    // row max over the tile, lazy reference update
-    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mt = across_rows<true>(mt) * c;
-    const bool need = mt > m + kHeadroom;
-    if (__any(need)) {
-      const float mnew = need ? mt : m;
-      const float alpha = (mnew == m) ? 1.f : fast_exp2(m - mnew);  // -inf -> 0
-      m = mnew;
-      l32 *= alpha;
+      for (int kb = 0; kb < KB; ++kb) s[r] = M::qk(bf.k[kb], qb[r][kb], s[r]);
+      if constexpr (!FULL) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = from_lane(alpha, 4 * g + i);  // O rows 4g+i live in lanes of row 4g+i
-#pragma unroll
-        for (int db = 0; db <= DB; ++db) acc[db][i] *= ai;
+        for (int i = 0; i < 4; ++i) s[r][i] = (tt + 4 * g + i < lim[r]) ? s[r][i] : -INFINITY;
       }
     }
-    float pr[4];
+    uint2 pa[NRB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[i] = fast_exp2(fmaf(s[i], c, -m));
-      if constexpr (!FULL) pr[i] = (s[i] == -INFINITY) ? 0.f : pr[i];
+    for (int r = 0; r < NRB; ++r) {
+      // row max over the tile, lazy reference update
+      float mt = fmaxf(fmaxf(s[r][0], s[r][1]), fmaxf(s[r][2], s[r][3]));
+      mt = across_rows<true>(mt) * c;
+      const bool need = mt > m[r] + kHeadroom;
+      if (__any(need)) {
+        const float mnew = need ? mt : m[r];
+        const float alpha = (mnew == m[r]) ? 1.f : fast_exp2(m[r] - mnew);  // -inf -> 0
+        m[r] = mnew;
+        l32[r] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = from_lane(alpha, 4 * g + i);  // O rows 4g+i live in lanes of row 4g+i
+#pragma unroll
+          for (int db = 0; db <= DB; ++db) acc[r][db][i] *= ai;
+        }
+      }
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = fast_exp2(fmaf(s[r][i], c, -m[r]));
+        if constexpr (!FULL) pr[i] = (s[r][i] == -INFINITY) ? 0.f : pr[i];
+      }
+      l32[r] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      pa[r] = make_uint2(M::pack(pr[0], pr[1]), M::pack(pr[2], pr[3]));
     }
-    l32 += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const uint2 pa = make_uint2(M::pack(pr[0], pr[1]), M::pack(pr[2], pr[3]));
-    // O += P . V, and the all-ones block for l
+    // O += P . V for each row block (one transposed read of V), and the
+    // all-ones block for l
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const s4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s4_ptr)(my_v + (kSwz ? v_rd_swz + ((db ^ i_rd) * 32) : v_rd + db * 32)));
-      acc[db] = M::pv(pa, __builtin_bit_cast(uint2, vt), acc[db]);
+#pragma unroll
+      for (int r = 0; r < NRB; ++r) acc[r][db] = M::pv(pa[r], __builtin_bit_cast(uint2, vt), acc[r][db]);
     }
-    acc[DB] = M::pv(pa, make_uint2(M::kOnePair, M::kOnePair), acc[DB]);
+#pragma unroll
+    for (int r = 0; r < NRB; ++r)
+      acc[r][DB] = M::pv(pa[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
   };
   auto process = [&](const Buf& bf, int idx) {
     const int tt = t0 + (wave + idx * NW) * kTile;
@@ -465,60 +492,65 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   const __amdgpu_buffer_rsrc_t r_lpart =
       make_rsrc(p.lse_part, uint32_t(min<long>((long)p.num_splits * p.nrows * 4, 0xFFFFFFFFl)));
 
-  // ---- merge the waves through LDS and write -----------------------------
+  // ---- merge the waves through LDS and write, one 16-row block at a time --
   // O layout: lane l holds rows 4g..4g+3, columns 16db + n16; l is acc[DB].
   // m of row r is held by lanes with n16 == r.
-  __syncthreads();  // the V staging area is reused below
   constexpr int RMAX = 16;
   float* s_acc = reinterpret_cast<float*>(s_buf);  // [NW][16][D]
   __shared__ float s_m[NW][RMAX];
   __shared__ float s_l[NW][RMAX];    // sums of the rounded probabilities (normalise O)
   __shared__ float s_l32[NW][RMAX];  // float32 sums (LSE)
-  l32 = across_rows<false>(l32);
-  const int rows_here = min(RMAX, rows_b - rb * 16);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i;
-    if (r < rows_here) {
+  for (int blk = 0; blk < NRB; ++blk) {
+    const int rows_here = min(RMAX, rows_b - row0 - 16 * blk);
+    if (rows_here <= 0) break;
+    __syncthreads();  // the V staging area (or the previous block) is reused below
+    const float l32b = across_rows<false>(l32[blk]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) s_acc[((long)wave * RMAX + r) * D + db * 16 + n16] = acc[db][i];
-      if (n16 == 0) s_l[wave][r] = acc[DB][i];
-    }
-  }
-  if (g == 0 && n16 < rows_here) {
-    s_m[wave][n16] = m;
-    s_l32[wave][n16] = l32;
-  }
-  __syncthreads();
-
-  for (int t = threadIdx.x; t < rows_here * hd; t += NW * 64) {
-    const int r = t / hd;
-    const int d = t % hd;
-    const int pr = rb * 16 + r;
-    float Mx = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      if (r < rows_here) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][r]);
-    float num = 0.f, den = 0.f, den32 = 0.f;
-    if (Mx != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = (s_m[w][r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - Mx);
-        num = fmaf(f, s_acc[((long)w * RMAX + r) * D + d], num);
-        den = fmaf(f, s_l[w][r], den);
-        den32 = fmaf(f, s_l32[w][r], den32);
+        for (int db = 0; db < DB; ++db)
+          s_acc[((long)wave * RMAX + r) * D + db * 16 + n16] = acc[blk][db][i];
+        if (n16 == 0) s_l[wave][r] = acc[blk][DB][i];
       }
     }
-    const float o = (Mx == -INFINITY) ? 0.f : num / den;
-    const float lse = (Mx == -INFINITY) ? -INFINITY : (Mx + log2f(den32)) * kLn2;
-    const int i = pr / p.heads_per_unit;
-    const int hq = hq0 + pr % p.heads_per_unit;
-    const long nrow = row_of(i, hq);
-    if (direct) {
-      static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(o);
-      if (d == 0 && p.lse) p.lse[lse_of(i, hq)] = lse;
-    } else {  // write-through stores: the merging workgroup may sit on another XCD
-      publish(r_opart, uint32_t(((long)split * p.nrows + nrow) * hd + d) * 4u, o);
-      if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, lse);
+    if (g == 0 && n16 < rows_here) {
+      s_m[wave][n16] = m[blk];
+      s_l32[wave][n16] = l32b;
+    }
+    __syncthreads();
+
+    for (int t = threadIdx.x; t < rows_here * hd; t += NW * 64) {
+      const int r = t / hd;
+      const int d = t % hd;
+      const int pr = row0 + 16 * blk + r;
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][r]);
+      float num = 0.f, den = 0.f, den32 = 0.f;
+      if (Mx != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = (s_m[w][r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - Mx);
+          num = fmaf(f, s_acc[((long)w * RMAX + r) * D + d], num);
+          den = fmaf(f, s_l[w][r], den);
+          den32 = fmaf(f, s_l32[w][r], den32);
+        }
+      }
+      const float o = (Mx == -INFINITY) ? 0.f : num / den;
+      const float lse = (Mx == -INFINITY) ? -INFINITY : (Mx + log2f(den32)) * kLn2;
+      const int i = pr / p.heads_per_unit;
+      const int hq = hq0 + pr % p.heads_per_unit;
+      const long nrow = row_of(i, hq);
+      if (direct) {
+        static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(o);
+        if (d == 0 && p.lse) p.lse[lse_of(i, hq)] = lse;
+      } else {  // write-through stores: the merging workgroup may sit on another XCD
+        publish(r_opart, uint32_t(((long)split * p.nrows + nrow) * hd + d) * 4u, o);
+        if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, lse);
+      }
     }
   }
   if (direct) return;
@@ -545,10 +577,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   __syncthreads();
   if (!s_last) return;
   const int S = nsplit;
-  for (int t = threadIdx.x; t < rows_here * hd; t += NW * 64) {
+  const int rows_unit = min(16 * NRB, rows_b - row0);
+  for (int t = threadIdx.x; t < rows_unit * hd; t += NW * 64) {
     const int r = t / hd;
     const int d = t % hd;
-    const int pr = rb * 16 + r;
+    const int pr = row0 + r;
     const int i = pr / p.heads_per_unit;
     const int hq = hq0 + pr % p.heads_per_unit;
     const long nrow = row_of(i, hq);
@@ -589,15 +622,26 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 
 // Waves per workgroup and tiles in flight per wave: 8 and 2 up to D = 128;
 // at D = 256 the accumulators and tiles leave room for one tile in flight
-// and the merge buffer for 4 waves; element loads at D = 128 also keep one
-// tile in flight (two would spill).
+// and the merge buffer for 4 waves; element loads, or two row blocks, at
+// D = 128 also keep one tile in flight (two would spill).
+template <int DT, int D, bool PAGED, int GEN, int NRB>
+hipError_t launch_mfma_k(const SplitParams& p, int grid, hipStream_t s) {
+  constexpr int NW = D <= 128 ? 8 : 4;
+  constexpr int NBUF = (D > 128 || (D == 128 && (GEN == 2 || NRB == 2))) ? 1 : 2;
+  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB>), dim3(grid),
+                     dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+// Two 16-row blocks per workgroup exist for the 16-byte-load kernels at head
+// dims 64 and 128 (the planner asks for them only there).
 template <int DT, int D, bool PAGED, int GEN>
 hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
-  constexpr int NW = D <= 128 ? 8 : 4;
-  constexpr int NBUF = (D > 128 || (GEN == 2 && D == 128)) ? 1 : 2;
-  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN>), dim3(grid), dim3(NW * 64),
-                     0, s, p);
-  return hipGetLastError();
+  if constexpr (GEN == 0 && (D == 64 || D == 128)) {
+    if (p.nrb == 2) return launch_mfma_k<DT, D, PAGED, GEN, 2>(p, grid, s);
+  }
+  if (p.nrb != 1) return hipErrorInvalidValue;
+  return launch_mfma_k<DT, D, PAGED, GEN, 1>(p, grid, s);
 }
 
 template <int DT, bool PAGED>

@@ -110,7 +110,11 @@ def test_plan_fields_are_consistent(lib):
     assert plan.workspace_bytes == 0 and plan.combine == 0
     # rows beyond 16 go to row blocks
     code, plan = _plan(lib, batch=2, q_len=3, hq=32, hkv=4, max_L=512, maxp=32, S=1, pack=1)
-    assert plan.rows_per_unit == 24 and plan.rows_per_block == 16 and plan.row_blocks == 2
+    assert plan.rows_per_unit == 24 and plan.rows_per_block == 32 and plan.row_blocks == 1
+    # two 16-row blocks per workgroup only where that kernel exists (d 64/128)
+    code, plan = _plan(lib, batch=2, q_len=3, hq=32, hkv=4, max_L=512, maxp=32, S=1, pack=1,
+                       d=96)
+    assert plan.rows_per_block == 16 and plan.row_blocks == 2
     # unpacked: one query head per unit
     code, plan = _plan(lib, batch=2, q_len=2, hq=8, hkv=2, max_L=512, maxp=32, S=1, pack=0)
     assert plan.rows_per_unit == 2 and plan.units == 2 * 8
