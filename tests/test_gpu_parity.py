@@ -271,6 +271,17 @@ def test_ragged_lengths_with_splits(lens, S):
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+@pytest.mark.parametrize("S", [257, 1024])
+def test_many_splits(S):
+    """Up to the largest split count a caller may ask for: 16 keys per split
+    at S = 1024, so the fused combine folds 1024 partials (64 batches)."""
+    wl = W.make_paged(1650 + S, "bf16", 2, 1, 8, 1, 128, 16, [16384, 9000], spare_pages=1)
+    ref = oracle_paged(wl)
+    case("many splits: B2 Hq8/Hkv1 d128 L=[16384, 9000], S=%d" % S)
+    plan = assert_paged(wl, num_splits=S, ref=ref)
+    assert plan.num_splits == S
+
+
 @pytest.mark.parametrize("B", [1024, 2048])
 def test_large_batches(B):
     """The largest batch that is ranked by length (1024) and one past it."""
