@@ -6,6 +6,7 @@ several 16-key tiles with ragged tails, GQA 1/2/4/8, q_len up to 8 (row
 blocks), head_dim 1..256, both dtypes, page sizes 16/32/48, empty sequences
 and NaN-poisoned slots outside the valid keys.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -465,6 +466,46 @@ def test_bitwise_determinism_and_page_permutation():
         a, la, _ = run_paged(wl, num_splits=S)
         b, lb, _ = run_paged(wl2, num_splits=S)
         assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_hip_graph_replays_match_eager():
+    """A split call (fused combine, arrival counters rearmed by the kernel,
+    no memset) captured in a HIP graph and replayed, with eager calls on
+    other inputs in between: every replay equals the eager result."""
+    wl = W.make_paged(1800, "bf16", 4, 2, 16, 4, 128, 16, [700, 33, 1500, 1], spare_pages=2)
+    q, kc, vc = to_dev(wl.q, "bf16"), to_dev(wl.k_cache, "bf16"), to_dev(wl.v_cache, "bf16")
+    bt, sl = i32_dev(wl.block_table), i32_dev(wl.cache_seqlens)
+    q2 = to_dev(W.make_paged(1801, "bf16", 4, 2, 16, 4, 128, 16, [700, 33, 1500, 1]).q, "bf16")
+    case("HIP graph capture of a 4-split decode call, 5 replays")
+    call = api.PreparedDecode(q, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
+                              max_seqlen_k=wl.max_seqlen_k)
+    other = api.PreparedDecode(q2, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
+                               max_seqlen_k=wl.max_seqlen_k)
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_l = bits_of(call.out).copy(), call.lse.cpu().numpy().copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the side stream, as graph capture wants
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    graph_call = api.PreparedDecode(q, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
+                                    max_seqlen_k=wl.max_seqlen_k, out=call.out, lse=call.lse,
+                                    workspace=call.workspace,
+                                    stream=None)
+    with torch.cuda.graph(g):
+        graph_call.args[-1] = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        graph_call()
+    for rep in range(5):
+        call.out.zero_()
+        other()  # eager work on the same workspace shape, other queries
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(call.out), ref_o), "replay %d" % rep
+        assert np.array_equal(call.lse.cpu().numpy(), ref_l), "replay %d" % rep
 
 
 def test_last_plan_matches_host_plan():
