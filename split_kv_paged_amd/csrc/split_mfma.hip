@@ -24,13 +24,18 @@
 //
 // K and V tiles move with 16-byte buffer loads into a ring of NBUF register
 // buffers: the loads of tile n+NBUF-1 are issued before tile n is computed.
+// For head_dim >= 64 (whole 16-byte chunks) eight lanes read one key row's
+// 128 contiguous bytes, so each load instruction touches whole cache lines;
+// both tiles then pass through the wave's LDS area (XOR-swizzled chunks) to
+// reach the MFMA operand layouts.
 // A buffer descriptor ends at the split's last key, so keys past it (another
 // split, the poisoned tail of a page, the end of a dense tensor) read as zero
 // without a fault.  The physical page of each tile comes from the block
 // table, 64 tiles' worth per vector load, broadcast with readlane.
 //
 // Packed query rows beyond the unit's real rows are zero; their lanes do the
-// same (SIMD) work and are never written.  A unit carries at most 16 rows.
+// same (SIMD) work and are never written.  A workgroup carries one or two
+// 16-row blocks (NRB) of one unit.
 //
 // Sources: attention definition (SmallQ FlashAttention README, section 接口);
 // online softmax with max offset (ai6s.net FlashAttention article, section
@@ -179,6 +184,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // a row), else padded by 32 bytes against bank clashes
   constexpr bool kSwz = D >= 64;
   constexpr int ROWB = kSwz ? D * 2 : D * 2 + 32;
+  // K is loaded with V's coalesced map (whole 128-byte lines per row) and
+  // read back from LDS in the MFMA operand layout
+  constexpr bool kKLds = kVCoal && kSwz;
   static_assert(D % 32 == 0, "head_dim");
   const int hd = GEN ? p.head_dim : D;  // elements per key / query / output row
 
@@ -346,10 +354,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 
   // V staging (NW x 16 padded key rows) during the loop; the same bytes
   // hold the waves' partial outputs (NW x 16 rows x D floats) for the merge.
-  constexpr int kStage = NW * kTile * ROWB;
+  constexpr int kStage = NW * kTile * ROWB * (kKLds ? 2 : 1);
   constexpr int kMerge = NW * 16 * D * 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[kStage > kMerge ? kStage : kMerge];
   uint8_t* const my_v = s_buf + wave * kTile * ROWB;
+  uint8_t* const my_k = s_buf + (NW + wave) * kTile * ROWB;  // (K staging, if used)
   typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
   const uint32_t v_wr = uint32_t(n16 * ROWB);  // row of this lane's V bytes (unswizzled)
   const int f_wr = 2 * (n16 & 3) + ((n16 >> 2) & 1);            // chunk XOR of row n16
@@ -398,11 +407,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       for (int kb = 0; kb < KB; ++kb) {
         const int ck = chunk(g, kb);
         const int off = (GEN == 0 || ck * 8 < hd) ? voff + ck * 16 : kPastEnd;
-        bf.k[kb] = load16(rk, off);
+        if constexpr (!kKLds) bf.k[kb] = load16(rk, off);
         if constexpr (kVCoal) {
           const int row_v = (lane >> 3) + 8 * (kb & 1), ch_v = (lane & 7) + 8 * (kb >> 1);
-          bf.v[kb] = load16(rv, (GEN == 0 || ch_v * 8 < hd)
-                                    ? int(row_v * row_stride * 2) + ch_v * 16 : kPastEnd);
+          const int off_v = (GEN == 0 || ch_v * 8 < hd)
+                                ? int(row_v * row_stride * 2) + ch_v * 16 : kPastEnd;
+          bf.v[kb] = load16(rv, off_v);
+          if constexpr (kKLds) bf.k[kb] = load16(rk, off_v);
         } else {
           bf.v[kb] = load16(rv, off);
         }
@@ -426,13 +437,28 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
         *reinterpret_cast<uint4*>(my_v + v_wr + chunk(g, kb) * 16) = bf.v[kb];
       }
     }
+    uint4 kq[KB];
+    if constexpr (kKLds) {  // K through LDS too: stage, then read in MFMA layout
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int row_v = (lane >> 3) + 8 * (kb & 1), ch_v = (lane & 7) + 8 * (kb >> 1);
+        const int f_v = 2 * (row_v & 3) + ((row_v >> 2) & 1);
+        *reinterpret_cast<uint4*>(my_k + row_v * ROWB + ((ch_v ^ f_v) * 16)) = bf.k[kb];
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        kq[kb] = *reinterpret_cast<const uint4*>(my_k + n16 * ROWB + ((chunk(g, kb) ^ f_wr) * 16));
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kq[kb] = bf.k[kb];
+    }
     // S^T = K . Q^T for each row block (one K tile, NRB query blocks)
     f4_t s[NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
       s[r] = (f4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[r] = M::qk(bf.k[kb], qb[r][kb], s[r]);
+      for (int kb = 0; kb < KB; ++kb) s[r] = M::qk(kq[kb], qb[r][kb], s[r]);
       if constexpr (!FULL) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[r][i] = (tt + 4 * g + i < lim[r]) ? s[r][i] : -INFINITY;
