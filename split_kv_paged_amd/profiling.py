@@ -59,11 +59,14 @@ def trace_rows(path):
 
 
 def kernel_resources(path):
-    """name -> (grid_x, workgroup_x, vgpr, agpr, sgpr, lds bytes) of the first dispatch."""
+    """name -> (grid_x, workgroup_x, lds bytes) of the first dispatch.
+
+    The register counts in the same table are left out: on gfx950 they follow
+    an allocation granule that differs from the code object's own
+    next-free-VGPR count, which is what limits occupancy."""
     con = sqlite3.connect(_db(path))
     out = {}
-    for r in con.execute("select name, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, "
-                         "sgpr_count, lds_size from kernels order by id"):
+    for r in con.execute("select name, grid_x, workgroup_x, lds_size from kernels order by id"):
         out.setdefault(r[0], r[1:])
     con.close()
     return out
@@ -111,9 +114,9 @@ def cmd_trace(a):
     if a.kernel:
         k = _pick([r[0] for r in rows], a.kernel)
         avg = next(r[3] for r in rows if r[0] == k)
-        g, wg, v, ag, s, lds = res.get(k, (0,) * 6)
-        lines += ["", "Kernel `%s`: grid %d threads, workgroup %d, %d VGPR + %d AGPR, %d SGPR, "
-                  "LDS %d bytes." % (_short(k, 120), g, wg, v, ag, s, lds)]
+        g, wg, lds = res.get(k, (0,) * 3)
+        lines += ["", "Kernel `%s`: grid %d threads, workgroup %d, LDS %d bytes."
+                  % (_short(k, 120), g, wg, lds)]
         if a.bytes:
             gbs = a.bytes / (avg * 1e-6) / 1e9
             lines += ["Algorithmic bytes per launch: %d. At the average duration: %.1f GB/s "
