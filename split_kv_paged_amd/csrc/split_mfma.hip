@@ -19,15 +19,17 @@
 //       sum of the rounded probabilities: O is divided by exactly the
 //       weights it was built from.  The LSE uses a float32 running sum of
 //       the unrounded probabilities.
-//       The V tile is staged in LDS by each wave and read back with
+//       The V tile sits in the wave's LDS slot and is read back with
 //       ds_read_b64_tr_b16, which delivers the key-major B operand.
 //
-// K and V tiles move with 16-byte buffer loads into a ring of NBUF register
-// buffers: the loads of tile n+NBUF-1 are issued before tile n is computed.
-// For head_dim >= 64 (whole 16-byte chunks) eight lanes read one key row's
-// 128 contiguous bytes, so each load instruction touches whole cache lines;
-// both tiles then pass through the wave's LDS area (XOR-swizzled chunks) to
-// reach the MFMA operand layouts.
+// Tile loads.  With 16-byte chunks and at least 8 of them a key row (head
+// dims 64..256, GEN 0/1), K and V go from memory straight into the wave's
+// LDS slot with 16-byte buffer loads to LDS: each instruction fills 1 KB,
+// whole key rows, so every load touches whole cache lines, and no register
+// holds a tile in flight.  A wave reads tile n out of its slot (K in the
+// MFMA A layout, V transposed), refills the slot with tile n+1, then
+// computes tile n.  The other kernels (head dim 32, or element loads) move
+// tiles through a ring of NBUF register buffers and stage V in LDS.
 // A buffer descriptor ends at the split's last key, so keys past it (another
 // split, the poisoned tail of a page, the end of a dense tensor) read as zero
 // without a fault.  The physical page of each tile comes from the block
@@ -173,20 +175,16 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // 128-byte line; any chunk order gives the same dot products as long as
   // Q uses it too).
   auto chunk = [](int g_, int kb_) { return kb_ * 4 + g_; };
-  // V only passes through LDS, so its loads need not follow the MFMA
-  // layout: 8 lanes read one whole 128-byte line of a row per instruction
-  // (rows 8 apart per instruction pair).  Measured on the paged GQA-4
-  // decode: 31.2 us with the MFMA layout for both, 29.7 with the chunk map
-  // above, 28.5 with both.
-  constexpr bool kVCoal = D >= 64 && GEN != 2;
-  // LDS bytes per staged V key row: unpadded with the 16-byte chunks of row
+  // LDS bytes per staged key row: unpadded with the 16-byte chunks of row
   // r permuted by XOR with f(r) = 2(r & 3) + ((r >> 2) & 1) (needs 8 chunks
   // a row), else padded by 32 bytes against bank clashes
   constexpr bool kSwz = D >= 64;
   constexpr int ROWB = kSwz ? D * 2 : D * 2 + 32;
-  // K is loaded with V's coalesced map (whole 128-byte lines per row) and
-  // read back from LDS in the MFMA operand layout
-  constexpr bool kKLds = kVCoal && kSwz;
+  // NBUF == 0: no register ring; each tile goes from memory straight into
+  // the wave's LDS slot, one tile in flight per wave while the previous one
+  // is computed
+  constexpr bool kDma = NBUF == 0;
+  static_assert(!kDma || (kSwz && GEN != 2), "direct-to-LDS tiles need >= 8 16-byte chunks a row");
   static_assert(D % 32 == 0, "head_dim");
   const int hd = GEN ? p.head_dim : D;  // elements per key / query / output row
 
@@ -282,10 +280,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // ---- Q^T as the B operand: lane l holds row l%16 of each 16-row block,
   // chunks g*KB + kb ------------------------------------------------------
   // Keys a lane's row may see: [t0, lim[r]).  Causal (bottom-right): query
-  // i of q_len sees keys j <= L - q_len + i.  Tiles below t_full need no
-  // mask in any row.
+  // i of q_len sees keys j <= L - q_len + i.  Every tile applies the mask
+  // (a few VALU ops); a separate unmasked copy of the tile code would make
+  // the compiler keep two copies of the accumulators live.
   int lim[NRB];
-  int t_full = t1;
 #pragma unroll
   for (int r = 0; r < NRB; ++r) lim[r] = t1;
   if (p.causal) {
@@ -294,7 +292,6 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       const int i_row = (row0 + 16 * r + n16) / p.heads_per_unit;
       lim[r] = min(t1, max(0, L - qlen_b + 1 + i_row));
     }
-    t_full = min(t1, max(0, L - qlen_b + 1));
   }
   auto row_of = [&](int i, int hq) -> long {
     return (long)(qbase + i) * p.n_si + (long)hq * p.n_sh;
@@ -352,13 +349,17 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(p.v);
   const int voff = int(n16 * row_stride * 2);  // key n16 of the tile
 
-  // V staging (NW x 16 padded key rows) during the loop; the same bytes
-  // hold the waves' partial outputs (NW x 16 rows x D floats) for the merge.
-  constexpr int kStage = NW * kTile * ROWB * (kKLds ? 2 : 1);
+  // Per-wave slots during the loop (V tile, then the K tile when it goes
+  // through LDS too); the same bytes hold the waves' partial outputs
+  // (NW x 16 rows x D floats) for the merge.
+  constexpr int kSlot = kTile * ROWB * (kDma ? 2 : 1);
+  constexpr int kStage = NW * kSlot;
   constexpr int kMerge = NW * 16 * D * 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[kStage > kMerge ? kStage : kMerge];
-  uint8_t* const my_v = s_buf + wave * kTile * ROWB;
-  uint8_t* const my_k = s_buf + (NW + wave) * kTile * ROWB;  // (K staging, if used)
+  // Each wave's K tile sits right after its V tile, so the two share
+  // address registers (a 4 KB immediate offset at D = 128).
+  uint8_t* const my_v = s_buf + wave * kSlot;
+  uint8_t* const my_k = my_v + kTile * ROWB;  // (direct-to-LDS tiles only)
   typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
   const uint32_t v_wr = uint32_t(n16 * ROWB);  // row of this lane's V bytes (unswizzled)
   const int f_wr = 2 * (n16 & 3) + ((n16 >> 2) & 1);            // chunk XOR of row n16
@@ -407,51 +408,16 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       for (int kb = 0; kb < KB; ++kb) {
         const int ck = chunk(g, kb);
         const int off = (GEN == 0 || ck * 8 < hd) ? voff + ck * 16 : kPastEnd;
-        if constexpr (!kKLds) bf.k[kb] = load16(rk, off);
-        if constexpr (kVCoal) {
-          const int row_v = (lane >> 3) + 8 * (kb & 1), ch_v = (lane & 7) + 8 * (kb >> 1);
-          const int off_v = (GEN == 0 || ch_v * 8 < hd)
-                                ? int(row_v * row_stride * 2) + ch_v * 16 : kPastEnd;
-          bf.v[kb] = load16(rv, off_v);
-          if constexpr (kKLds) bf.k[kb] = load16(rk, off_v);
-        } else {
-          bf.v[kb] = load16(rv, off);
-        }
+        bf.k[kb] = load16(rk, off);
+        bf.v[kb] = load16(rv, off);
       }
     }
   };
 
   const float c = p.scale_log2;
-  auto process_tile = [&](const Buf& bf, int tt, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    // stage V (row-major, padded rows) for the transposed reads
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if constexpr (kVCoal) {
-        const int row_v = (lane >> 3) + 8 * (kb & 1), ch_v = (lane & 7) + 8 * (kb >> 1);
-        const int f_v = 2 * (row_v & 3) + ((row_v >> 2) & 1);
-        *reinterpret_cast<uint4*>(my_v + row_v * ROWB + ((ch_v ^ f_v) * 16)) = bf.v[kb];
-      } else if constexpr (kSwz) {
-        *reinterpret_cast<uint4*>(my_v + n16 * ROWB + ((chunk(g, kb) ^ f_wr) * 16)) = bf.v[kb];
-      } else {
-        *reinterpret_cast<uint4*>(my_v + v_wr + chunk(g, kb) * 16) = bf.v[kb];
-      }
-    }
-    uint4 kq[KB];
-    if constexpr (kKLds) {  // K through LDS too: stage, then read in MFMA layout
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int row_v = (lane >> 3) + 8 * (kb & 1), ch_v = (lane & 7) + 8 * (kb >> 1);
-        const int f_v = 2 * (row_v & 3) + ((row_v >> 2) & 1);
-        *reinterpret_cast<uint4*>(my_k + row_v * ROWB + ((ch_v ^ f_v) * 16)) = bf.k[kb];
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        kq[kb] = *reinterpret_cast<const uint4*>(my_k + n16 * ROWB + ((chunk(g, kb) ^ f_wr) * 16));
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kq[kb] = bf.k[kb];
-    }
+  // Scores, online softmax and P.V of one tile: kq holds this lane's K
+  // operand chunks, vop(db) returns the V operand of d block db.
+  auto tile_math = [&](const uint4 (&kq)[KB], auto vop, int tt) {
     // S^T = K . Q^T for each row block (one K tile, NRB query blocks)
     f4_t s[NRB];
 #pragma unroll
@@ -459,10 +425,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       s[r] = (f4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[r] = M::qk(kq[kb], qb[r][kb], s[r]);
-      if constexpr (!FULL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[r][i] = (tt + 4 * g + i < lim[r]) ? s[r][i] : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) s[r][i] = (tt + 4 * g + i < lim[r]) ? s[r][i] : -INFINITY;
     }
     uint2 pa[NRB];
 #pragma unroll
@@ -487,39 +451,97 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pr[i] = fast_exp2(fmaf(s[r][i], c, -m[r]));
-        if constexpr (!FULL) pr[i] = (s[r][i] == -INFINITY) ? 0.f : pr[i];
+        pr[i] = (s[r][i] == -INFINITY) ? 0.f : pr[i];
       }
       l32[r] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       pa[r] = make_uint2(M::pack(pr[0], pr[1]), M::pack(pr[2], pr[3]));
     }
-    // O += P . V for each row block (one transposed read of V), and the
+    // O += P . V for each row block (one V operand per d block), and the
     // all-ones block for l
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const s4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_ptr)(my_v + (kSwz ? v_rd_swz + ((db ^ i_rd) * 32) : v_rd + db * 32)));
+      const uint2 vt = vop(db);
 #pragma unroll
-      for (int r = 0; r < NRB; ++r) acc[r][db] = M::pv(pa[r], __builtin_bit_cast(uint2, vt), acc[r][db]);
+      for (int r = 0; r < NRB; ++r) acc[r][db] = M::pv(pa[r], vt, acc[r][db]);
     }
 #pragma unroll
     for (int r = 0; r < NRB; ++r)
       acc[r][DB] = M::pv(pa[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
   };
+  // transposed read of d block db of the wave's staged V tile
+  auto v_tr = [&](int db) -> uint2 {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4_ptr)(my_v + (kSwz ? v_rd_swz + ((db ^ i_rd) * 32) : v_rd + db * 32))));
+  };
+  auto process_tile = [&](const Buf& bf, int tt) {
+    // stage V (row-major) for the transposed reads
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (kSwz) {
+        *reinterpret_cast<uint4*>(my_v + n16 * ROWB + ((chunk(g, kb) ^ f_wr) * 16)) = bf.v[kb];
+      } else {
+        *reinterpret_cast<uint4*>(my_v + v_wr + chunk(g, kb) * 16) = bf.v[kb];
+      }
+    }
+    tile_math(bf.k, v_tr, tt);
+  };
+  // Direct-to-LDS issue of tile idx: 1 KB per instruction, lane l landing
+  // at byte 16 l of it, so lane l fetches the global chunk that the
+  // swizzled layout puts there (row r's chunk c sits at c ^ f(r)).
+  constexpr int kCPR = ROWB / 16;    // 16-byte chunks per staged row
+  constexpr int kRPI = 1024 / ROWB;  // rows per load instruction
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto issue_dma = [&](int idx, int page) {
+    page = __builtin_amdgcn_readfirstlane(page);
+    const int tt = t0 + (wave + idx * NW) * kTile;
+    const long row0 = tile_row0(idx, page);
+    const uint32_t bytes = uint32_t(min(kTile, t1 - tt) * row_stride * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0, bytes);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int row = j * kRPI + lane / kCPR;
+      const int ch = (lane % kCPR) ^ (2 * (row & 3) + ((row >> 2) & 1));
+      const int off = (GEN == 0 || ch * 8 < hd) ? int(row * row_stride * 2) + ch * 16 : kPastEnd;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(my_k + j * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(my_v + j * 1024), 16, off, 0, 0, 0);
+    }
+  };
   auto process = [&](const Buf& bf, int idx) {
     const int tt = t0 + (wave + idx * NW) * kTile;
-    if (tt + kTile <= t_full)
-      process_tile(bf, tt, std::true_type{});
-    else
-      process_tile(bf, tt, std::false_type{});
+    process_tile(bf, tt);
   };
 
-  // ---- main loop: NBUF tiles in a register ring --------------------------
+  // ---- main loop ----------------------------------------------------------
+  if constexpr (kDma) {
+    // s_waitcnt immediates: vmcnt(0) alone, lgkmcnt(0) alone
+    constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
+    for (int cb = 0; cb < my_tiles; cb += 64) {
+      if (cb > 0) pages = load_pages(cb);
+      const int n = min(64, my_tiles - cb);
+      auto page_at = [&](int i) { return __builtin_amdgcn_readlane(pages, i); };
+      issue_dma(cb, page_at(0));
+      for (int i = 0; i < n; ++i) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // tile i has landed in the slot
+        uint4 kq[KB];
+        uint2 vt[DB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          kq[kb] = *reinterpret_cast<const uint4*>(my_k + n16 * ROWB + ((chunk(g, kb) ^ f_wr) * 16));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vt[db] = v_tr(db);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot is read out before it is refilled
+        if (i + 1 < n) issue_dma(cb + i + 1, page_at(i + 1));
+        tile_math(kq, [&](int db) { return vt[db]; }, t0 + (wave + (cb + i) * NW) * kTile);
+      }
+    }
+  } else {  // NBUF tiles in a register ring
   for (int cb = 0; cb < my_tiles; cb += 64) {
     if (cb > 0) pages = load_pages(cb);
     const int n = min(64, my_tiles - cb);
     const int last = n - 1;
     auto page_at = [&](int i) { return __builtin_amdgcn_readlane(pages, i); };
-    Buf ring[NBUF];
+    Buf ring[NBUF > 0 ? NBUF : 1];
 #pragma unroll
     for (int k = 0; k < NBUF - 1; ++k) issue(ring[k], cb + min(k, last), page_at(min(k, last)));
     int i = 0;
@@ -535,6 +557,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
         }
       }
     }
+  }
   }
 
   // partial buffers of a split call (the host keeps them below 4 GiB)
@@ -671,14 +694,19 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Waves per workgroup and tiles in flight per wave: 8 and 2 up to D = 128;
-// at D = 256 the accumulators and tiles leave room for one tile in flight
-// and the merge buffer for 4 waves; element loads, or two row blocks, at
-// D = 128 also keep one tile in flight (two would spill).
+// Waves per workgroup: 8 up to D = 128, 4 at D = 256 (accumulators and
+// the merge buffer).  Tiles of 16-byte chunks with at least 8 chunks a row
+// go straight to LDS (NBUF = 0).  The others use a register ring: two
+// tiles per wave up to D = 64, one above (two would spill).
+// Measured, ring against direct-to-LDS (paged bf16 GQA-4 decode, d 128):
+// 28.2 vs 27.4 us; with 32 query rows per unit (causal q_len 8): 37.2 vs
+// 34.7 us.  Direct-to-LDS with 16 waves, or two tiles per wave step, was
+// slower (28.2 and 28.1 us).
 template <int DT, int D, bool PAGED, int GEN, int NRB>
 hipError_t launch_mfma_k(const SplitParams& p, int grid, hipStream_t s) {
+  constexpr bool kDirect = GEN != 2 && D >= 64;
   constexpr int NW = D <= 128 ? 8 : 4;
-  constexpr int NBUF = (D > 128 || (D == 128 && (GEN == 2 || NRB == 2))) ? 1 : 2;
+  constexpr int NBUF = kDirect ? 0 : D >= 128 ? 1 : 2;
   hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB>), dim3(grid),
                      dim3(NW * 64), 0, s, p);
   return hipGetLastError();
