@@ -36,6 +36,8 @@ def parse():
                          "c2: dense fp16 MHA 32 heads qLen4 d128 (--kv-len)")
     ap.add_argument("--kv-len", type=int, default=4096, help="c2 only")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = planner")
+    ap.add_argument("--no-length-sum", action="store_true",
+                    help="paged: do not give the planner the sum of the lengths")
     ap.add_argument("--pools", type=int, default=4, help="KV pool copies rotated over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -93,13 +95,18 @@ def main():
         bt = torch.from_numpy(wl.block_table).to(dev)
         sl = torch.from_numpy(wl.cache_seqlens).to(dev)
         lse = torch.empty((wl.batch, wl.num_heads_q, wl.q_len), dtype=torch.float32, device=dev)
+        # a serving loop knows its lengths on the host; their sum lets the
+        # planner split the longest sequences of a ragged batch
+        hint = None if args.no_length_sum else int(wl.cache_seqlens.sum())
         first = api.PreparedDecode(q, pools[0][0], pools[0][1], bt, sl,
                                    num_splits=args.num_splits, softmax_scale=wl.scale,
-                                   max_seqlen_k=wl.max_seqlen_k, out=out, lse=lse, stream=stream)
+                                   max_seqlen_k=wl.max_seqlen_k, out=out, lse=lse, stream=stream,
+                                   sum_seqlen_k=hint)
         calls = [first] + [api.PreparedDecode(q, kc, vc, bt, sl, num_splits=args.num_splits,
                                               softmax_scale=wl.scale,
                                               max_seqlen_k=wl.max_seqlen_k, out=out, lse=lse,
-                                              workspace=first.workspace, stream=stream)
+                                              workspace=first.workspace, stream=stream,
+                                              sum_seqlen_k=hint)
                            for kc, vc in pools[1:]]
 
     def step(i):
@@ -149,7 +156,8 @@ def main():
         config = {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len,
                   "num_heads_q": wl.num_heads_q, "num_heads_kv": wl.num_heads_kv,
                   "head_dim": wl.head_dim, "page_size": wl.page_size,
-                  "kv_tokens": int(wl.cache_seqlens.sum())}
+                  "kv_tokens": int(wl.cache_seqlens.sum()),
+                  "length_sum_given": not args.no_length_sum}
     config.update({"kv_bytes": kv_bytes, "num_splits": last.num_splits,
                    "pack_gqa": last.pack_gqa, "grid": last.grid, "kv_pools": len(pools),
                    "accumulate": "f32"})

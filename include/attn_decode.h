@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
     ATTN_OK = 0,
@@ -88,6 +88,14 @@ typedef struct {
     int32_t max_pages_per_seq;
     int32_t max_seqlen_k;  /* upper bound of cache_seqlens; drives the plan   */
     int32_t dtype;         /* attn_dtype                                       */
+    int64_t sum_seqlen_k;  /* optional: sum of cache_seqlens (0 = not given).
+                            * With it, an automatic plan (num_splits 0) also
+                            * splits a ragged batch whose longest sequence
+                            * exceeds two compute units' fair shares of all
+                            * keys, into pieces of at most half a share (an
+                            * addition to the pages' rule).  0 <= sum <=
+                            * batch * max_seqlen_k, else ATTN_ERR_SHAPE; a
+                            * wrong but in-range value changes only speed. */
 } attn_decode_shape;
 
 /* Dense small-query problem (the SmallQ README's [heads, qLen, headDim]

@@ -29,22 +29,25 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
-def decode_shape(q, k_cache, block_table, max_seqlen_k=None):
+def decode_shape(q, k_cache, block_table, max_seqlen_k=None, sum_seqlen_k=None):
     B, qlen, hq, d = q.shape
     _, page, hkv, d2 = k_cache.shape
     _need(d2 == d, "q and k_cache head_dim differ")
     maxp = block_table.shape[1]
     if max_seqlen_k is None:
         max_seqlen_k = maxp * page
-    return _L.DecodeShape(B, qlen, hq, hkv, d, page, maxp, int(max_seqlen_k), _DT[q.dtype])
+    return _L.DecodeShape(B, qlen, hq, hkv, d, page, maxp, int(max_seqlen_k), _DT[q.dtype],
+                          int(sum_seqlen_k or 0))
 
 
 def decode_plan(batch, q_len, num_heads_q, num_heads_kv, head_dim, page_size, max_pages_per_seq,
-                max_seqlen_k, dtype=torch.bfloat16, num_splits=0, pack_gqa=-1, num_cus=0):
+                max_seqlen_k, dtype=torch.bfloat16, num_splits=0, pack_gqa=-1, num_cus=0,
+                sum_seqlen_k=0):
     """Host-only plan (no device touched)."""
     shape = _L.DecodeShape(batch, q_len, num_heads_q, num_heads_kv, head_dim, page_size,
                            max_pages_per_seq, max_seqlen_k,
-                           _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype))
+                           _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+                           int(sum_seqlen_k))
     plan = _L.Plan()
     _L.check("attn_decode_plan",
              _L.load().attn_decode_plan(ctypes.byref(shape), num_splits, pack_gqa, num_cus,
@@ -81,7 +84,8 @@ def _check_dev(*ts):
 
 def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pack_gqa=-1,
                softmax_scale=None, max_seqlen_k=None, out=None, lse=None, return_lse=True,
-               workspace=None, stream=None, k_new=None, v_new=None, causal=False):
+               workspace=None, stream=None, k_new=None, v_new=None, causal=False,
+               sum_seqlen_k=None):
     """Paged decode attention.
 
     q [B, q_len, Hq, d] fp16/bf16; k_cache, v_cache [pages, page, Hkv, d];
@@ -92,13 +96,15 @@ def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pa
     k_new / v_new [B, new_len, Hkv, d]: keys written into the cache at
     positions cache_seqlens[b].. before attention (attn_decode_kvcache_fwd);
     causal: query i of q_len sees keys j <= L - q_len + i.
+    sum_seqlen_k (optional host int, the sum of the attended lengths) lets
+    an automatic plan split the longest sequences of a ragged batch.
     """
     _need(q.dtype in _DT and k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
           "q, k_cache, v_cache must share fp16 or bf16")
     _need(block_table.dtype == torch.int32 and cache_seqlens.dtype == torch.int32,
           "block_table and cache_seqlens must be int32")
     dev = _check_dev(q, k_cache, v_cache, block_table, cache_seqlens, out, lse, workspace)
-    shape = decode_shape(q, k_cache, block_table, max_seqlen_k)
+    shape = decode_shape(q, k_cache, block_table, max_seqlen_k, sum_seqlen_k)
     lib = _L.load()
     plan = _L.Plan()
     with torch.cuda.device(dev):
@@ -144,7 +150,7 @@ def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pa
 def decode_varlen_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
                       max_seqlen_q, num_splits=0, softmax_scale=None, max_seqlen_k=None,
                       out=None, lse=None, return_lse=True, workspace=None, stream=None,
-                      k_new=None, v_new=None, causal=False):
+                      k_new=None, v_new=None, causal=False, sum_seqlen_k=None):
     """Paged decode attention with a query count per sequence.
 
     q [total_q, Hq, d]; cu_seqlens_q int32 [B + 1] on the device (queries of
@@ -164,7 +170,7 @@ def decode_varlen_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlen
     maxp = block_table.shape[1]
     shape = _L.DecodeShape(B, int(max_seqlen_q), hq, hkv, d, page, maxp,
                            int(max_seqlen_k if max_seqlen_k is not None else maxp * page),
-                           _DT[q.dtype])
+                           _DT[q.dtype], int(sum_seqlen_k or 0))
     lib = _L.load()
     plan = _L.Plan()
     new_len = 0
@@ -285,11 +291,11 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0,
                  pack_gqa=-1, softmax_scale=None, max_seqlen_k=None, out=None, lse=None,
-                 workspace=None, stream=None, causal=False):
+                 workspace=None, stream=None, causal=False, sum_seqlen_k=None):
         _need(q.dtype in _DT and k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
               "q, k_cache, v_cache must share fp16 or bf16")
         dev = _check_dev(q, k_cache, v_cache, block_table, cache_seqlens, out, lse, workspace)
-        self.shape = decode_shape(q, k_cache, block_table, max_seqlen_k)
+        self.shape = decode_shape(q, k_cache, block_table, max_seqlen_k, sum_seqlen_k)
         self.lib = _L.load()
         plan = _L.Plan()
         cus = torch.cuda.get_device_properties(dev).multi_processor_count

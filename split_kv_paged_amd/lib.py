@@ -29,7 +29,7 @@ EXPORTS = (
 class DecodeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "q_len", "num_heads_q", "num_heads_kv", "head_dim", "page_size",
-        "max_pages_per_seq", "max_seqlen_k", "dtype")]
+        "max_pages_per_seq", "max_seqlen_k", "dtype")] + [("sum_seqlen_k", ctypes.c_int64)]
 
 
 class DenseShape(ctypes.Structure):

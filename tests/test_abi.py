@@ -54,7 +54,8 @@ def test_status_strings(lib):
 
 def _plan(lib, **kw):
     shape = L.DecodeShape(kw["batch"], kw["q_len"], kw["hq"], kw["hkv"], kw.get("d", 128),
-                          kw.get("page", 16), kw.get("maxp", 64), kw["max_L"], kw.get("dt", 1))
+                          kw.get("page", 16), kw.get("maxp", 64), kw["max_L"], kw.get("dt", 1),
+                          kw.get("sum_L", 0))
     plan = L.Plan()
     code = lib.attn_decode_plan(ctypes.byref(shape), kw.get("S", 0), kw.get("pack", -1),
                                 kw.get("cus", 0), ctypes.byref(plan))
@@ -241,3 +242,53 @@ def test_check_paged_inputs(lib):
     assert api.check_paged_inputs(args, bt, np.array([1, 0], np.int32), 7) == \
         ("ATTN_ERR_DATA", 0)
     assert api.check_paged_inputs(args, bt, np.array([0, 0], np.int32), 7) == ("ATTN_OK", -1)
+
+
+# The ragged-batch refinement (not from the pages): with the sum of the
+# lengths given, the planner takes max(page rule, ceil(max_L / (share / 2)))
+# when max_L > 2 * share, share = streams * sum_L / CUs, streams = head units
+# x row blocks.  Expected values worked by hand for the shapes below.
+RAGGED_CASES = [
+    # (name, kwargs, expected S)
+    # 128 seqs, 16 q heads / 8 KV heads, d 64: share = 8 * 112861 / 256 =
+    # 3526.9; 7769 > 7053.8; ceil(7769 / 1763.45) = 5; page rule alone: 1
+    ("ragged d64", dict(batch=128, q_len=1, hq=16, hkv=8, d=64, maxp=512, max_L=7769,
+                        sum_L=112861), 5),
+    # 32 seqs GQA-4 d 128: share = 8 * 40957 / 256 = 1279.9; ceil(6642 / 639.95) = 11
+    ("ragged d128", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=416, max_L=6642, sum_L=40957), 11),
+    # near-uniform lengths: share = 8 * 32002 / 256 = 1000.06; 1100 <= 2000: rule's 1
+    ("uniform ~1000", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=69, max_L=1100, sum_L=32002), 1),
+    # long uniform context: share 2048, 16384 > 4096: ceil(16384 / 1024) = 16 over the rule's 14
+    ("long uniform", dict(batch=4, q_len=1, hq=32, hkv=8, maxp=1024, max_L=16384, sum_L=65536), 16),
+    # one long sequence among 255 one-key ones: 510 pieces asked, capped at 128
+    ("cap", dict(batch=256, q_len=1, hq=1, hkv=1, maxp=4096, max_L=65536, sum_L=65536 + 255), 128),
+    # 32 query rows per unit (q_len 8, G 4): two row blocks of 16 would be one
+    # 32-row block, streams = 8: share = 8 * 40957 / 256, as in "ragged d128"
+    ("ragged 32 rows", dict(batch=32, q_len=8, hq=32, hkv=8, maxp=416, max_L=6642,
+                            sum_L=40957), 11),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", RAGGED_CASES, ids=[c[0] for c in RAGGED_CASES])
+def test_ragged_hint_plan(lib, name, kw, want):
+    code, plan = _plan(lib, **kw)
+    assert L.STATUS[code] == "ATTN_OK"
+    assert plan.num_splits == want, (name, plan.num_splits)
+    # without the hint the pages' rule alone decides
+    kw0 = dict(kw, sum_L=0)
+    code0, plan0 = _plan(lib, **kw0)
+    ref_splits, _ = oplan.plan(kw["batch"], kw["q_len"], kw["hq"], kw["hkv"], kw["max_L"], 256,
+                               16, 128)
+    assert plan0.num_splits == ref_splits
+    assert plan.num_splits >= plan0.num_splits
+
+
+def test_ragged_hint_rejects_out_of_range(lib):
+    base = dict(batch=4, q_len=1, hq=8, hkv=2, maxp=64, max_L=1000)
+    assert L.STATUS[_plan(lib, **base, sum_L=-1)[0]] == "ATTN_ERR_SHAPE"
+    assert L.STATUS[_plan(lib, **base, sum_L=4001)[0]] == "ATTN_ERR_SHAPE"
+    assert L.STATUS[_plan(lib, **base, sum_L=4000)[0]] == "ATTN_OK"
+    # an explicit split count is never changed by the hint
+    code, plan = _plan(lib, batch=128, q_len=1, hq=16, hkv=8, d=64, maxp=512, max_L=7769,
+                       sum_L=112861, S=3)
+    assert L.STATUS[code] == "ATTN_OK" and plan.num_splits == 3

@@ -26,7 +26,7 @@ def case(msg):
     sys.stdout.flush()
 
 
-def run_paged(wl, num_splits=0, pack_gqa=-1, workspace=None):
+def run_paged(wl, num_splits=0, pack_gqa=-1, workspace=None, sum_hint=False):
     q = to_dev(wl.q, wl.dtype)
     kc = to_dev(wl.k_cache, wl.dtype)
     vc = to_dev(wl.v_cache, wl.dtype)
@@ -34,7 +34,8 @@ def run_paged(wl, num_splits=0, pack_gqa=-1, workspace=None):
     sl = i32_dev(wl.cache_seqlens)
     out, lse = api.decode_fwd(q, kc, vc, bt, sl, num_splits=num_splits, pack_gqa=pack_gqa,
                               softmax_scale=wl.scale, max_seqlen_k=max(wl.max_seqlen_k, 0),
-                              workspace=workspace)
+                              workspace=workspace,
+                              sum_seqlen_k=int(wl.cache_seqlens.sum()) if sum_hint else None)
     torch.cuda.synchronize()
     return bits_of(out), lse.cpu().numpy(), api.last_plan()
 
@@ -270,6 +271,37 @@ def test_ragged_lengths_with_splits(lens, S):
     a, la, _ = run_paged(wl, num_splits=S)
     b, lb, _ = run_paged(wl, num_splits=S)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("spec", [
+    ("bf16", 32, 1, 32, 8, 128),   # log-uniform lengths 1..8192, GQA-4 d 128
+    ("fp16", 128, 1, 16, 8, 64),   # the same at 128 sequences, GQA-2 d 64
+    ("bf16", 32, 8, 32, 8, 128),   # 32 query rows per unit (one 32-row block), causal
+])
+def test_ragged_batch_with_length_sum_hint(spec):
+    """With the sum of the lengths given, the automatic plan splits the
+    longest sequences of a ragged batch (S > 1, per-sequence split counts)
+    and the result still matches the oracle."""
+    dt, B, qlen, hq, hkv, d = spec
+    causal = qlen > 1
+    wl = W.make_paged(1750 + B + qlen, dt, B, qlen, hq, hkv, d, 16,
+                      lambda rng: W.c5_lengths(rng, batch=B), spare_pages=1)
+    case("ragged %s B%d q%d Hq%d/Hkv%d d%d with the length-sum hint" % spec)
+    q = to_dev(wl.q, dt)
+    kc, vc = to_dev(wl.k_cache, dt), to_dev(wl.v_cache, dt)
+    bt, sl = i32_dev(wl.block_table), i32_dev(wl.cache_seqlens)
+    out, lse = api.decode_fwd(q, kc, vc, bt, sl, softmax_scale=wl.scale,
+                              max_seqlen_k=wl.max_seqlen_k, causal=causal,
+                              sum_seqlen_k=int(wl.cache_seqlens.sum()))
+    torch.cuda.synchronize()
+    plan = api.last_plan()
+    assert plan.num_splits > 1
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    e1 = check_out(bits_of(out), ref_o, dt, wl.name)
+    e2 = check_lse(lse.cpu().numpy(), ref_l)
+    print("  plan S=%d grid=%d  max|dO|=%.3g max|dLSE|=%.3g" % (plan.num_splits, plan.grid, e1, e2),
+          flush=True)
 
 
 @pytest.mark.parametrize("S", [257, 1024])
