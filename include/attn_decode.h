@@ -90,9 +90,10 @@ typedef struct {
     int32_t dtype;         /* attn_dtype                                       */
     int64_t sum_seqlen_k;  /* optional: sum of cache_seqlens (0 = not given).
                             * With it, an automatic plan (num_splits 0) also
-                            * splits a ragged batch whose longest sequence
-                            * exceeds two compute units' fair shares of all
-                            * keys, into pieces of at most half a share (an
+                            * splits a ragged batch (max_seqlen_k over twice
+                            * the mean length) whose longest sequence exceeds
+                            * two compute units' fair shares of all keys,
+                            * into pieces of at most half a share (an
                             * addition to the pages' rule).  0 <= sum <=
                             * batch * max_seqlen_k, else ATTN_ERR_SHAPE; a
                             * wrong but in-range value changes only speed. */

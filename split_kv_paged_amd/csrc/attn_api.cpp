@@ -66,18 +66,22 @@ int num_splits_rule(int64_t total_mblocks, int num_cus, int64_t num_n_blocks) {
 // Ragged batches (not from the pages; their rule sees only max_seqlen_k).
 // Given the sum of the batch's lengths, a compute unit's fair share of the
 // job is streams * sum / num_cus keys, streams being the KV passes per
-// sequence (head units x row blocks).  When the longest sequence exceeds two
-// shares it would outlast the rest of the batch on one workgroup, so it is
+// sequence (head units x row blocks).  In a ragged batch (longest sequence
+// over twice the mean) whose longest sequence also exceeds two shares, that
+// sequence would outlast the rest of the batch on one workgroup, so it is
 // cut into pieces of at most half a share; shorter sequences keep fewer
-// splits (a split past a sequence's end does nothing).  Returns the split
-// count this asks for (1 when the batch is not ragged enough), at most
+// splits (a split past a sequence's end does nothing).  Uniform batches are
+// left to the pages' rule, which already sizes splits by the common length.
+// Returns the split count this asks for (1 when it does not apply), at most
 // kMaxSplitsRule.  Measured on MI355X (paged, 8 KV heads): 128 sequences of
 // log-uniform length 1..8192 at d 64, 81.7 us at S = 1 and 62.9 at S = 5
 // (this rule's pick); 32 such sequences at d 128, 79.0 and 46.0 (S = 11).
-int ragged_splits(int64_t streams, int64_t sum_seqlen_k, int64_t max_seqlen_k, int num_cus) {
-  if (sum_seqlen_k <= 0 || streams <= 0) return 1;
+int ragged_splits(int64_t batch, int64_t streams, int64_t sum_seqlen_k, int64_t max_seqlen_k,
+                  int num_cus) {
+  if (sum_seqlen_k <= 0 || streams <= 0 || batch <= 0) return 1;
+  const double mean = double(sum_seqlen_k) / double(batch);
   const double share = double(streams) * double(sum_seqlen_k) / double(num_cus);
-  if (double(max_seqlen_k) <= 2.0 * share) return 1;
+  if (double(max_seqlen_k) <= 2.0 * mean || double(max_seqlen_k) <= 2.0 * share) return 1;
   const double s = std::ceil(double(max_seqlen_k) / (0.5 * share));
   return s >= kMaxSplitsRule ? kMaxSplitsRule : int(s);
 }
@@ -116,7 +120,7 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
     splits = num_splits_rule(total, num_cus, ceil_div(max_seqlen_k, kBlockN));
     const int64_t rpb0 = (rows > kRowsPerBlock && (head_dim == 64 || head_dim == 128))
                              ? 2 * kRowsPerBlock : kRowsPerBlock;
-    splits = std::max(splits, ragged_splits(heads * ceil_div(rows, rpb0), sum_seqlen_k,
+    splits = std::max(splits, ragged_splits(batch, heads * ceil_div(rows, rpb0), sum_seqlen_k,
                                             max_seqlen_k, num_cus));
   }
   if (splits > 1) pack = true;  // same article, section "常见坑点"

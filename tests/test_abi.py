@@ -246,8 +246,9 @@ def test_check_paged_inputs(lib):
 
 # The ragged-batch refinement (not from the pages): with the sum of the
 # lengths given, the planner takes max(page rule, ceil(max_L / (share / 2)))
-# when max_L > 2 * share, share = streams * sum_L / CUs, streams = head units
-# x row blocks.  Expected values worked by hand for the shapes below.
+# when max_L > 2 * mean and max_L > 2 * share, share = streams * sum_L / CUs,
+# streams = head units x row blocks.  Expected values worked by hand for the
+# shapes below.
 RAGGED_CASES = [
     # (name, kwargs, expected S)
     # 128 seqs, 16 q heads / 8 KV heads, d 64: share = 8 * 112861 / 256 =
@@ -258,8 +259,12 @@ RAGGED_CASES = [
     ("ragged d128", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=416, max_L=6642, sum_L=40957), 11),
     # near-uniform lengths: share = 8 * 32002 / 256 = 1000.06; 1100 <= 2000: rule's 1
     ("uniform ~1000", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=69, max_L=1100, sum_L=32002), 1),
-    # long uniform context: share 2048, 16384 > 4096: ceil(16384 / 1024) = 16 over the rule's 14
-    ("long uniform", dict(batch=4, q_len=1, hq=32, hkv=8, maxp=1024, max_L=16384, sum_L=65536), 16),
+    # long uniform context, GQA-8: max_L = mean, not ragged: the rule's 14
+    ("long uniform", dict(batch=4, q_len=1, hq=32, hkv=4, maxp=1024, max_L=16384, sum_L=65536), 14),
+    # ragged but short against the share: mean 1000, max 2400 > 2000, share
+    # 8 * 64000 / 256 = 2000, 2400 <= 4000: the rule's 1
+    ("ragged under two shares", dict(batch=64, q_len=1, hq=32, hkv=8, maxp=150, max_L=2400,
+                                     sum_L=64000), 1),
     # one long sequence among 255 one-key ones: 510 pieces asked, capped at 128
     ("cap", dict(batch=256, q_len=1, hq=1, hkv=1, maxp=4096, max_L=65536, sum_L=65536 + 255), 128),
     # 32 query rows per unit (q_len 8, G 4): two row blocks of 16 would be one
