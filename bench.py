@@ -134,6 +134,22 @@ def main():
     launch_ms = ev_start.elapsed_time(ev_end) / K
     last = api.last_plan()
 
+    # Spread of single launches (outside the timed region): an event pair
+    # around each of up to 100 launches.  The host then paces the launches,
+    # so each starts on an idle GPU; the average above stays the figure.
+    n_one = min(K, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_one)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    one = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+    def pct(q):
+        return round(one[min(n_one - 1, int(q * (n_one - 1) + 0.5))], 3)
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -193,6 +209,8 @@ def main():
             "kernel_avg_us": round(kern_s * 1e6, 3),
             "kernels_per_launch": 1,
         },
+        "single_launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "n": n_one,
+                             "method": "event pair around each launch, host-paced"},
     }
     if cpu is not None:
         rec["cpu_baseline"] = cpu
@@ -236,12 +254,22 @@ def cpu_baseline(wl, budget_s):
         if time.perf_counter() - t_start > budget_s or len(times) >= 20:
             break
     t = float(np.median(times))
+    # one run on one thread, beside the all-threads median
+    t1 = time.perf_counter()
+    if dense:
+        oracle.dense_attention(wl.q, wl.k, wl.v, wl.dtype, scale=wl.scale, nthreads=1)
+    else:
+        oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                               wl.cache_seqlens, wl.dtype, scale=wl.scale, nthreads=1)
+    t1 = time.perf_counter() - t1
     rows = wl.q_len * wl.num_heads_q * (1 if dense else wl.batch)
     keys = wl.kv_len if dense else int(wl.cache_seqlens.sum())
     return {"value": round(wl.kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "whole workload (%d query rows, %d keys), %d repetitions, median %.3f s"
-                      % (rows, keys, len(times), t)}
+                      % (rows, keys, len(times), t),
+            "single_thread_value": round(wl.kv_bytes / t1 / 1e9, 4),
+            "host_threads": os.cpu_count()}
 
 
 if __name__ == "__main__":
