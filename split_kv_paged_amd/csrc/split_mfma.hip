@@ -29,7 +29,8 @@
 // holds a tile in flight.  A wave reads tile n out of its slot (K in the
 // MFMA A layout, V transposed), refills the slot with tile n+1, then
 // computes tile n.  The other kernels (head dim 32, or element loads) move
-// tiles through a ring of NBUF register buffers and stage V in LDS.
+// tiles through a ring of NBUF register buffers and stage V in LDS.  Every
+// K/V load is non-temporal: each KV byte is read once per call.
 // A buffer descriptor ends at the split's last key, so keys past it (another
 // split, the poisoned tail of a page, the end of a dense tensor) read as zero
 // without a fault.  The physical page of each tile comes from the block
@@ -110,13 +111,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
 }
 
+// Cache policy of every K/V tile load: non-temporal (CPol::NT).  Each KV
+// byte is read once per call, so keeping it in L2 only evicts what is worth
+// keeping.  Measured (paged GQA-4 bf16 decode / uniform L 4000 / long
+// context S = 14 / ragged S = 5, us): 27.5 / 93.0 / 32.0 / 64.0 with the
+// default policy, 25.7 / 84.7 / 29.8 / 59.7 with NT.
+constexpr int kStream = 2;
+
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, kStream));
 }
 
 // a 16-bit element (zero-extended); offsets past the descriptor's range read 0
 __device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, int voffset) {
-  return uint32_t(__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voffset, 0, 0)));
+  return uint32_t(
+      __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voffset, 0, kStream)));
 }
 constexpr int kPastEnd = 0x7FFFFFF0;  // beyond any tile's range (tiles are < 2 GiB)
 
@@ -503,8 +512,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       const int row = j * kRPI + lane / kCPR;
       const int ch = (lane % kCPR) ^ (2 * (row & 3) + ((row >> 2) & 1));
       const int off = (GEN == 0 || ch * 8 < hd) ? int(row * row_stride * 2) + ch * 16 : kPastEnd;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(my_k + j * 1024), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(my_v + j * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(my_k + j * 1024), 16, off, 0, 0, kStream);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(my_v + j * 1024), 16, off, 0, 0, kStream);
     }
   };
   auto process = [&](const Buf& bf, int idx) {
