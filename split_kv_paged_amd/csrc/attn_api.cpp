@@ -63,6 +63,17 @@ int num_splits_rule(int64_t total_mblocks, int num_cus, int64_t num_n_blocks) {
   return 1;
 }
 
+// Packed rows one workgroup carries: 16 (one MFMA row block); where the
+// kernels exist (16-byte loads), 32 for units of more than 16 rows at head
+// dims 64 and 128, and 64 for units of more than 32 rows at head dim 64,
+// so a workgroup reads its KV once for all of them.
+int rows_per_block(int64_t rows, int head_dim) {
+  if (head_dim != 64 && head_dim != 128) return kRowsPerBlock;
+  if (rows > 2 * kRowsPerBlock && head_dim == 64) return 4 * kRowsPerBlock;
+  if (rows > kRowsPerBlock) return 2 * kRowsPerBlock;
+  return kRowsPerBlock;
+}
+
 // Ragged batches (not from the pages; their rule sees only max_seqlen_k).
 // Given the sum of the batch's lengths, a compute unit's fair share of the
 // job is streams * sum / num_cus keys, streams being the KV passes per
@@ -118,19 +129,14 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
     const int64_t rows = pack ? int64_t(q_len) * group : q_len;
     const int64_t total = batch * heads * ceil_div(rows, kBlockM);
     splits = num_splits_rule(total, num_cus, ceil_div(max_seqlen_k, kBlockN));
-    const int64_t rpb0 = (rows > kRowsPerBlock && (head_dim == 64 || head_dim == 128))
-                             ? 2 * kRowsPerBlock : kRowsPerBlock;
+    const int64_t rpb0 = rows_per_block(rows, head_dim);
     splits = std::max(splits, ragged_splits(batch, heads * ceil_div(rows, rpb0), sum_seqlen_k,
                                             max_seqlen_k, num_cus));
   }
   if (splits > 1) pack = true;  // same article, section "常见坑点"
 
   const int64_t rows_per_unit = pack ? int64_t(q_len) * group : q_len;
-  // more than 16 rows: two 16-row blocks per workgroup (the KV is read once
-  // for 32 rows), where that kernel exists (16-byte loads, head dim 64/128)
-  const int rpb = (rows_per_unit > kRowsPerBlock && (head_dim == 64 || head_dim == 128))
-                      ? 2 * kRowsPerBlock
-                      : kRowsPerBlock;
+  const int rpb = rows_per_block(rows_per_unit, head_dim);
   const int64_t row_blocks = ceil_div(rows_per_unit, rpb);
   const int64_t unit_heads = pack ? hkv : hq;
   const int64_t units = batch * unit_heads * row_blocks;

@@ -33,7 +33,7 @@ struct SplitParams {
   int split_keys;      // keys per split (multiple of 16); split s = [s*C, (s+1)*C)
   int rows;            // valid rows per unit (q_len * heads_per_unit)
   int row_blocks;      // ceil(rows / (16 * nrb))
-  int nrb;             // 16-row blocks per workgroup (1 or 2)
+  int nrb;             // 16-row blocks per workgroup (1, 2 or 4)
   int heads_per_unit;  // group (packed) or 1
   int unit_heads;      // Hkv (packed) or Hq
   int nrows;           // batch * q_len * Hq

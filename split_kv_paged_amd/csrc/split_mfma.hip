@@ -85,6 +85,10 @@ struct Mf<1> {  // bfloat16
   static __device__ __forceinline__ uint16_t round(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
+  // the two values of a packed pair, exactly, as floats
+  static __device__ __forceinline__ f2_t widen(uint32_t v) {
+    return (f2_t){__builtin_bit_cast(float, v << 16), __builtin_bit_cast(float, v & 0xFFFF0000u)};
+  }
   static constexpr uint32_t kOnePair = 0x3F803F80u;
 };
 
@@ -103,6 +107,9 @@ struct Mf<0> {  // IEEE binary16
   }
   static __device__ __forceinline__ uint16_t round(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static __device__ __forceinline__ f2_t widen(uint32_t v) {
+    return __builtin_convertvector(__builtin_bit_cast(h2_t, v), f2_t);
   }
   static constexpr uint32_t kOnePair = 0x3C003C00u;
 };
@@ -171,8 +178,8 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
 //   1  head_dim a multiple of 8 (rows stay 16-byte aligned): 16-byte loads,
 //      a chunk past the head dim gets an offset past the buffer range;
 //   2  any other head_dim: 16-bit element loads.
-// NRB: 16-row blocks a workgroup carries (1, or 2 when a unit has more
-// than 16 packed rows, so its KV is read once for 32 rows).
+// NRB: 16-row blocks a workgroup carries (1; 2 or 4 when a unit has more
+// than 16 or 32 packed rows, so its KV is read once for up to 64 rows).
 template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB>
 __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
   using M = Mf<DT>;
@@ -424,6 +431,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   };
 
   const float c = p.scale_log2;
+  // bfloat16 probabilities carry 8 significant bits: rounded once, their
+  // relative error (2^-9) times large, cancelling V rows can exceed the
+  // output tolerance (seen at 0.06 with 8x outlier rows over 700 keys).
+  // There P goes in as two bfloat16 operands, the rounded value and its
+  // residue (16 bits together), for P.V and for the row sums; the MFMA
+  // work doubles, a few percent of the launch.  fp16's 11 bits need no
+  // residue.
+  constexpr bool kSplitP = DT == 1;
   // Scores, online softmax and P.V of one tile: kq holds this lane's K
   // operand chunks, vop(db) returns the V operand of d block db.
   auto tile_math = [&](const uint4 (&kq)[KB], auto vop, int tt) {
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[r][i] = (tt + 4 * g + i < lim[r]) ? s[r][i] : -INFINITY;
     }
-    uint2 pa[NRB];
+    uint2 pa[NRB], pl[NRB];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
       // row max over the tile, lazy reference update
@@ -464,6 +479,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       }
       l32[r] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       pa[r] = make_uint2(M::pack(pr[0], pr[1]), M::pack(pr[2], pr[3]));
+      if constexpr (kSplitP) {  // the rounding residue, as a second operand
+        const f2_t h01 = M::widen(pa[r].x), h23 = M::widen(pa[r].y);
+        pl[r] = make_uint2(M::pack(pr[0] - h01[0], pr[1] - h01[1]),
+                           M::pack(pr[2] - h23[0], pr[3] - h23[1]));
+      }
     }
     // O += P . V for each row block (one V operand per d block), and the
     // all-ones block for l
@@ -471,11 +491,17 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     for (int db = 0; db < DB; ++db) {
       const uint2 vt = vop(db);
 #pragma unroll
-      for (int r = 0; r < NRB; ++r) acc[r][db] = M::pv(pa[r], vt, acc[r][db]);
+      for (int r = 0; r < NRB; ++r) {
+        acc[r][db] = M::pv(pa[r], vt, acc[r][db]);
+        if constexpr (kSplitP) acc[r][db] = M::pv(pl[r], vt, acc[r][db]);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < NRB; ++r)
+    for (int r = 0; r < NRB; ++r) {
       acc[r][DB] = M::pv(pa[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
+      if constexpr (kSplitP)
+        acc[r][DB] = M::pv(pl[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
+    }
   };
   // transposed read of d block db of the wave's staged V tile
   auto v_tr = [&](int db) -> uint2 {
@@ -722,11 +748,17 @@ hipError_t launch_mfma_k(const SplitParams& p, int grid, hipStream_t s) {
 }
 
 // Two 16-row blocks per workgroup exist for the 16-byte-load kernels at head
-// dims 64 and 128 (the planner asks for them only there).
+// dims 64 and 128, four at 64 (the planner asks for them only there).  Four
+// at d 128 would need 4 waves of one per SIMD for the accumulators; that
+// halves the bytes in flight and measured no faster than two 32-row
+// workgroups (53.6 vs 53.0 us, GQA-8 q_len 8).
 template <int DT, int D, bool PAGED, int GEN>
 hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
   if constexpr (GEN == 0 && (D == 64 || D == 128)) {
     if (p.nrb == 2) return launch_mfma_k<DT, D, PAGED, GEN, 2>(p, grid, s);
+  }
+  if constexpr (GEN == 0 && D == 64) {
+    if (p.nrb == 4) return launch_mfma_k<DT, D, PAGED, GEN, 4>(p, grid, s);
   }
   if (p.nrb != 1) return hipErrorInvalidValue;
   return launch_mfma_k<DT, D, PAGED, GEN, 1>(p, grid, s);

@@ -180,10 +180,14 @@ def test_paged_any_head_dim(d):
 CAUSAL = [
     # dtype, B, qlen, Hq, Hkv, d, lens
     ("bf16", 3, 4, 32, 8, 128, [2, 4, 300]),     # GQA 4: 16 rows; L < q_len; L = q_len
-    ("fp16", 2, 8, 16, 2, 64, [9, 129]),         # GQA 8: 64 rows -> 4 row blocks
+    ("fp16", 2, 8, 16, 2, 64, [9, 129]),         # GQA 8 d 64: one 64-row block
     ("bf16", 2, 2, 8, 8, 128, [1, 77]),          # MHA, one query sees nothing in b 0
     ("fp16", 2, 3, 8, 4, 96, [40, 1000]),        # any head dim
     ("bf16", 2, 5, 8, 1, 64, [17, 18]),          # MQA, 40 rows
+    ("bf16", 2, 8, 64, 8, 128, [33, 700]),       # GQA 8 d 128: 64 rows, two 32-row blocks
+    ("fp16", 2, 6, 64, 8, 128, [1, 500]),        # 48 rows: the second block half empty
+    ("bf16", 2, 12, 64, 8, 128, [30, 400]),      # 96 rows: three 32-row blocks
+    ("bf16", 2, 6, 48, 8, 64, [200, 900]),       # d 64, G 6: 36 rows in one 64-row block
 ]
 
 
