@@ -346,13 +346,20 @@ def test_large_batches(B):
 
 # ------------------------------------------------------------- varlen Q ----
 
+VARLEN = [
+    # dtype, Hq, Hkv, d, q lens
+    ("bf16", 16, 4, 128, [1, 4, 0, 7, 2]),   # G 4: up to 28 rows (a 32-row block)
+    ("fp16", 32, 4, 64, [6, 1, 5, 0, 8]),    # G 8: up to 64 rows (a 64-row block)
+]
+
+
+@pytest.mark.parametrize("shape", VARLEN, ids=lambda v: "%s-G%d-d%d" % (v[0], v[1] // v[2], v[3]))
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("S", [0, 1, 3])
-def test_varlen_queries(causal, S):
+def test_varlen_queries(shape, causal, S):
     """A query count per sequence (cu_seqlens_q), packed; each sequence's
     expected rows come from the oracle run on that sequence alone."""
-    dt, hq, hkv, d = "bf16", 16, 4, 128
-    qlens = [1, 4, 0, 7, 2]
+    dt, hq, hkv, d, qlens = shape
     lens = [30, 300, 64, 9, 1000]
     B, maxq = len(lens), max(qlens)
     wl = W.make_paged(1400 + S, dt, B, maxq, hq, hkv, d, 16, lens, spare_pages=2)
@@ -390,8 +397,8 @@ SMALL = [
     ("fp16", 4, 1, 4, 4, 64, 32, [31, 32, 33, 95]),
     ("bf16", 2, 2, 8, 2, 128, 16, [40, 129]),      # qlen 2, G 4: 8 rows
     ("fp16", 2, 3, 8, 4, 64, 16, [77, 3]),          # 6 rows -> R 8 with 2 idle rows
-    ("bf16", 2, 4, 16, 4, 128, 32, [200, 64]),      # 16 rows -> 2 row blocks
-    ("fp16", 1, 8, 8, 1, 128, 16, [300]),           # 64 rows -> 8 row blocks, MQA
+    ("bf16", 2, 4, 16, 4, 128, 32, [200, 64]),      # 16 rows: one 16-row block
+    ("fp16", 1, 8, 8, 1, 128, 16, [300]),           # MQA, 64 rows: two 32-row blocks
     ("bf16", 5, 1, 8, 8, 128, 16, [1, 2, 3, 16, 17]),  # MHA
     ("fp16", 2, 1, 24, 3, 64, 48, [500, 1000]),     # G 8, page 48
 ]
