@@ -431,14 +431,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   };
 
   const float c = p.scale_log2;
-  // bfloat16 probabilities carry 8 significant bits: rounded once, their
-  // relative error (2^-9) times large, cancelling V rows can exceed the
-  // output tolerance (seen at 0.06 with 8x outlier rows over 700 keys).
-  // There P goes in as two bfloat16 operands, the rounded value and its
-  // residue (16 bits together), for P.V and for the row sums; the MFMA
-  // work doubles, a few percent of the launch.  fp16's 11 bits need no
-  // residue.
-  constexpr bool kSplitP = DT == 1;
+  // A 16-bit probability rounded once has a relative error up to 2^-9
+  // (bfloat16) or 2^-12 (fp16); times large, cancelling V rows that can
+  // exceed the output tolerance (seen at 0.06 in bf16 and 0.015 in fp16
+  // with 8x outlier K/V rows).  So P goes in as two 16-bit operands, the
+  // rounded value and its residue (16 or 22 significant bits together),
+  // for P.V and for the row sums; the MFMA work doubles, about 1% of the
+  // launch.
+  constexpr bool kSplitP = true;
   // Scores, online softmax and P.V of one tile: kq holds this lane's K
   // operand chunks, vop(db) returns the V operand of d block db.
   auto tile_math = [&](const uint4 (&kq)[KB], auto vop, int tt) {

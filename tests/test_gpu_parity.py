@@ -110,16 +110,17 @@ def test_ragged_fp16_outliers_full_size():
     assert_paged(wl, num_splits=8, ref=ref)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("S", [1, 4])
-def test_paged_bf16_outliers_full_size(S):
-    """The paged GQA-4 bf16 shape with 1% of K/V rows scaled by 8: large,
-    cancelling P.V terms, where bfloat16 probabilities rounded once fall
-    outside the tolerance (the kernel adds their residue)."""
+def test_paged_outliers_full_size(dt, S):
+    """The paged GQA-4 d 128 shape with 1% of K/V rows scaled by 8: large,
+    cancelling P.V terms, where 16-bit probabilities rounded once fall
+    outside the tolerance in both types (the kernel adds their residue)."""
     rng = np.random.default_rng(1003)
     lens = [int(x) for x in rng.integers(900, 1101, 32)]
-    wl = W.make_paged(1903, "bf16", 32, 1, 32, 8, 128, 16, lens, spare_pages=1, outlier_p=0.01)
-    case("paged bf16 B32 GQA-4 d128 L~1000, 1%% outliers x8 (%d rows), S=%d"
-         % (wl.meta["outlier_rows"], S))
+    wl = W.make_paged(1903, dt, 32, 1, 32, 8, 128, 16, lens, spare_pages=1, outlier_p=0.01)
+    case("paged %s B32 GQA-4 d128 L~1000, 1%% outliers x8 (%d rows), S=%d"
+         % (dt, wl.meta["outlier_rows"], S))
     assert_paged(wl, num_splits=S)
 
 
