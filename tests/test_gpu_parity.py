@@ -596,3 +596,41 @@ def test_scale_override():
     wl = W.make_paged(841, "bf16", 2, 1, 8, 2, 128, 16, [60, 90], spare_pages=1, scale=0.37)
     case("softmax_scale=0.37")
     assert_paged(wl)
+
+
+# --------------------------------------------------------- seeded mixtures --
+
+def _random_config(k):
+    """Configuration k of a fixed, seeded mixture over dtype, head dim (with
+    padded and element-load dims), GQA, q_len, causal, batch, log-uniform
+    lengths, outlier rows and split count."""
+    rng = np.random.default_rng(9000 + k)
+    dt = ["bf16", "fp16"][rng.integers(2)]
+    d = int(rng.choice([32, 64, 80, 96, 100, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    qlen = int(rng.choice([1, 1, 2, 4, 8]))
+    causal = bool(qlen > 1 and rng.integers(2))
+    B = int(rng.integers(1, 7))
+    lens = [int(x) for x in np.exp(rng.uniform(0, np.log(3000), B)).astype(int)]
+    outl = float(rng.choice([0.0, 0.01, 0.05]))
+    S = int(rng.choice([0, 1, 3, 8]))
+    return dt, d, hkv, G, qlen, causal, B, lens, outl, S
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_seeded_mixture(k):
+    dt, d, hkv, G, qlen, causal, B, lens, outl, S = _random_config(k)
+    wl = W.make_paged(9100 + k, dt, B, qlen, hkv * G, hkv, d, 16, lens, spare_pages=1,
+                      outlier_p=outl)
+    case("mixture %d: %s d%d Hkv%d G%d q%d causal=%s B%d L=%s outliers=%g S=%d"
+         % (k, dt, d, hkv, G, qlen, causal, B, lens, outl, S))
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    out, lse = api.decode_fwd(to_dev(wl.q, dt), to_dev(wl.k_cache, dt), to_dev(wl.v_cache, dt),
+                              i32_dev(wl.block_table), i32_dev(wl.cache_seqlens), num_splits=S,
+                              softmax_scale=wl.scale, max_seqlen_k=max(wl.max_seqlen_k, 0),
+                              causal=causal)
+    torch.cuda.synchronize()
+    check_out(bits_of(out), ref_o, dt)
+    check_lse(lse.cpu().numpy(), ref_l)
