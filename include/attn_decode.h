@@ -121,10 +121,9 @@ typedef struct {
     int32_t num_splits;      /* S: KV ranges per (sequence, head unit)        */
     int32_t pack_gqa;        /* 1: the G query heads of a KV head share a unit */
     int32_t rows_per_unit;   /* query rows per unit: q_len*G packed, q_len not */
-    int32_t rows_per_block;  /* packed rows one workgroup carries: 16; 32 for  */
-                             /* units of more than 16 rows at head_dim 64 or   */
-                             /* 128; 64 beyond 32 rows at head_dim 64 (the KV  */
-                             /* is read once per block)                        */
+    int32_t rows_per_block;  /* packed rows one workgroup carries: 16; at      */
+                             /* head_dim 64 or 128, 32 for units of 17..32     */
+                             /* rows and 64 beyond (KV read once per block)    */
     int32_t row_blocks;      /* ceil(rows_per_unit / rows_per_block)           */
     int32_t units;           /* batch * head units * row_blocks               */
     int32_t grid;            /* workgroups of the split kernel = units * S    */

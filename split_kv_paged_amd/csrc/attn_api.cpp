@@ -64,12 +64,12 @@ int num_splits_rule(int64_t total_mblocks, int num_cus, int64_t num_n_blocks) {
 }
 
 // Packed rows one workgroup carries: 16 (one MFMA row block); where the
-// kernels exist (16-byte loads), 32 for units of more than 16 rows at head
-// dims 64 and 128, and 64 for units of more than 32 rows at head dim 64,
-// so a workgroup reads its KV once for all of them.
+// kernels exist (16-byte loads at head dims 64 and 128), 32 for units of
+// more than 16 rows and 64 beyond 32, so a workgroup reads its KV once for
+// all of them.
 int rows_per_block(int64_t rows, int head_dim) {
   if (head_dim != 64 && head_dim != 128) return kRowsPerBlock;
-  if (rows > 2 * kRowsPerBlock && head_dim == 64) return 4 * kRowsPerBlock;
+  if (rows > 2 * kRowsPerBlock) return 4 * kRowsPerBlock;
   if (rows > kRowsPerBlock) return 2 * kRowsPerBlock;
   return kRowsPerBlock;
 }

@@ -315,9 +315,31 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   auto lse_of = [&](int i, int hq) -> long {
     return p.cu_q ? (long)hq * p.total_q + qbase + i : ((long)b * p.hq + hq) * p.q_len + i;
   };
-  uint4 qb[NRB][KB];
+  // Q^T operands.  Four row blocks at D = 128 would need 64 more VGPRs than
+  // eight waves have next to their accumulators, so there the workgroup
+  // stages its 64 query rows in LDS once (16-byte chunks of row r at
+  // c ^ f(r), as for K) and each wave reads a row block's operand per tile.
+  constexpr bool kQLds = NRB == 4 && D == 128;
+  static_assert(!kQLds || GEN == 0, "staged Q rows are whole 16-byte chunks");
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[kQLds ? 16 * NRB * D * 2 : 16];
+  if constexpr (kQLds) {
+    constexpr int kChunks = 16 * NRB * (D / 8);  // 16-byte chunks of the 64 rows
+    for (int ci = threadIdx.x; ci < kChunks; ci += NW * 64) {
+      const int rr = ci / (D / 8), cc = ci % (D / 8);
+      const int rowq = row0 + rr;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rowq < rows_b) {
+        const long n = row_of(rowq / p.heads_per_unit, hq0 + rowq % p.heads_per_unit);
+        v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd)[cc];
+      }
+      const int f = 2 * (rr & 3) + ((rr >> 2) & 1);
+      *reinterpret_cast<uint4*>(s_q + rr * (D * 2) + ((cc ^ f) * 16)) = v;
+    }
+    __syncthreads();
+  }
+  uint4 qb[kQLds ? 1 : NRB][KB];
 #pragma unroll
-  for (int r = 0; r < NRB; ++r) {
+  for (int r = 0; r < (kQLds ? 0 : NRB); ++r) {
     const int rowq = row0 + 16 * r + n16;  // packed row of this lane in block r of S^T
     bool real = rowq < rows_b;
     long n = 0;
@@ -434,10 +456,12 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // A 16-bit probability rounded once has a relative error up to 2^-9
   // (bfloat16) or 2^-12 (fp16); times large, cancelling V rows that can
   // exceed the output tolerance (seen at 0.06 in bf16 and 0.015 in fp16
-  // with 8x outlier K/V rows).  So P goes in as two 16-bit operands, the
-  // rounded value and its residue (16 or 22 significant bits together),
-  // for P.V and for the row sums; the MFMA work doubles, about 1% of the
-  // launch.
+  // with 8x outlier K/V rows).  So P goes in as the rounded value plus the
+  // rounding of its residue (16 or 22 significant bits together), for P.V
+  // and for the row sums, in one 16x16x32 product per block: a lane's 8
+  // k-values are its 4 keys' rounded P and their 4 residues (A), against
+  // its 4 V values twice (B).  Same key order as the 16x16x16 layout, so no
+  // lane exchange.
   constexpr bool kSplitP = true;
   // Scores, online softmax and P.V of one tile: kq holds this lane's K
   // operand chunks, vop(db) returns the V operand of d block db.
@@ -448,7 +472,15 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     for (int r = 0; r < NRB; ++r) {
       s[r] = (f4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[r] = M::qk(kq[kb], qb[r][kb], s[r]);
+      for (int kb = 0; kb < KB; ++kb) {
+        uint4 qv;
+        if constexpr (kQLds)  // row 16r + n16 has the chunk XOR of row n16
+          qv = *reinterpret_cast<const uint4*>(s_q + (16 * r + n16) * (D * 2) +
+                                               ((chunk(g, kb) ^ f_wr) * 16));
+        else
+          qv = qb[r][kb];
+        s[r] = M::qk(kq[kb], qv, s[r]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[r][i] = (tt + 4 * g + i < lim[r]) ? s[r][i] : -INFINITY;
     }
@@ -492,15 +524,23 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       const uint2 vt = vop(db);
 #pragma unroll
       for (int r = 0; r < NRB; ++r) {
-        acc[r][db] = M::pv(pa[r], vt, acc[r][db]);
-        if constexpr (kSplitP) acc[r][db] = M::pv(pl[r], vt, acc[r][db]);
+        if constexpr (kSplitP) {
+          acc[r][db] = M::qk(make_uint4(pa[r].x, pa[r].y, pl[r].x, pl[r].y),
+                             make_uint4(vt.x, vt.y, vt.x, vt.y), acc[r][db]);
+        } else {
+          acc[r][db] = M::pv(pa[r], vt, acc[r][db]);
+        }
       }
     }
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-      acc[r][DB] = M::pv(pa[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
-      if constexpr (kSplitP)
-        acc[r][DB] = M::pv(pl[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
+      if constexpr (kSplitP) {
+        acc[r][DB] = M::qk(make_uint4(pa[r].x, pa[r].y, pl[r].x, pl[r].y),
+                           make_uint4(M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair),
+                           acc[r][DB]);
+      } else {
+        acc[r][DB] = M::pv(pa[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
+      }
     }
   };
   // transposed read of d block db of the wave's staged V tile
@@ -747,17 +787,15 @@ hipError_t launch_mfma_k(const SplitParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Two 16-row blocks per workgroup exist for the 16-byte-load kernels at head
-// dims 64 and 128, four at 64 (the planner asks for them only there).  Four
-// at d 128 would need 4 waves of one per SIMD for the accumulators; that
-// halves the bytes in flight and measured no faster than two 32-row
-// workgroups (53.6 vs 53.0 us, GQA-8 q_len 8).
+// Two or four 16-row blocks per workgroup exist for the 16-byte-load
+// kernels at head dims 64 and 128 (the planner asks for them only there);
+// four at 128 read Q from LDS.
 template <int DT, int D, bool PAGED, int GEN>
 hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
   if constexpr (GEN == 0 && (D == 64 || D == 128)) {
     if (p.nrb == 2) return launch_mfma_k<DT, D, PAGED, GEN, 2>(p, grid, s);
   }
-  if constexpr (GEN == 0 && D == 64) {
+  if constexpr (GEN == 0 && (D == 64 || D == 128)) {
     if (p.nrb == 4) return launch_mfma_k<DT, D, PAGED, GEN, 4>(p, grid, s);
   }
   if (p.nrb != 1) return hipErrorInvalidValue;

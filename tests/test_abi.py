@@ -112,16 +112,16 @@ def test_plan_fields_are_consistent(lib):
     # rows beyond 16 go to row blocks
     code, plan = _plan(lib, batch=2, q_len=3, hq=32, hkv=4, max_L=512, maxp=32, S=1, pack=1)
     assert plan.rows_per_unit == 24 and plan.rows_per_block == 32 and plan.row_blocks == 1
-    # beyond 32 rows: 64-row blocks at d 64, 32-row blocks at d 128
+    # beyond 32 rows: 64-row blocks (d 64 and 128)
     code, plan = _plan(lib, batch=2, q_len=8, hq=64, hkv=8, max_L=512, maxp=32, S=1, pack=1, d=64)
     assert plan.rows_per_unit == 64 and plan.rows_per_block == 64 and plan.row_blocks == 1
     code, plan = _plan(lib, batch=2, q_len=5, hq=8, hkv=1, max_L=512, maxp=32, S=1, pack=1, d=64)
     assert plan.rows_per_unit == 40 and plan.rows_per_block == 64 and plan.row_blocks == 1
     code, plan = _plan(lib, batch=2, q_len=8, hq=64, hkv=8, max_L=512, maxp=32, S=1, pack=1)
-    assert plan.rows_per_unit == 64 and plan.rows_per_block == 32 and plan.row_blocks == 2
+    assert plan.rows_per_unit == 64 and plan.rows_per_block == 64 and plan.row_blocks == 1
     code, plan = _plan(lib, batch=2, q_len=12, hq=64, hkv=8, max_L=512, maxp=32, S=1, pack=1)
-    assert plan.rows_per_unit == 96 and plan.rows_per_block == 32 and plan.row_blocks == 3
-    assert plan.units == 2 * 8 * 3 and plan.grid == plan.units
+    assert plan.rows_per_unit == 96 and plan.rows_per_block == 64 and plan.row_blocks == 2
+    assert plan.units == 2 * 8 * 2 and plan.grid == plan.units
     # two 16-row blocks per workgroup only where that kernel exists (d 64/128)
     code, plan = _plan(lib, batch=2, q_len=3, hq=32, hkv=4, max_L=512, maxp=32, S=1, pack=1,
                        d=96)

@@ -198,9 +198,9 @@ CAUSAL = [
     ("bf16", 2, 2, 8, 8, 128, [1, 77]),          # MHA, one query sees nothing in b 0
     ("fp16", 2, 3, 8, 4, 96, [40, 1000]),        # any head dim
     ("bf16", 2, 5, 8, 1, 64, [17, 18]),          # MQA, 40 rows
-    ("bf16", 2, 8, 64, 8, 128, [33, 700]),       # GQA 8 d 128: 64 rows, two 32-row blocks
-    ("fp16", 2, 6, 64, 8, 128, [1, 500]),        # 48 rows: the second block half empty
-    ("bf16", 2, 12, 64, 8, 128, [30, 400]),      # 96 rows: three 32-row blocks
+    ("bf16", 2, 8, 64, 8, 128, [33, 700]),       # GQA 8 d 128: one 64-row block (Q in LDS)
+    ("fp16", 2, 6, 64, 8, 128, [1, 500]),        # 48 rows: a 64-row block, 16 rows empty
+    ("bf16", 2, 12, 64, 8, 128, [30, 400]),      # 96 rows: two 64-row blocks, one half empty
     ("bf16", 2, 6, 48, 8, 64, [200, 900]),       # d 64, G 6: 36 rows in one 64-row block
 ]
 
@@ -399,7 +399,7 @@ SMALL = [
     ("bf16", 2, 2, 8, 2, 128, 16, [40, 129]),      # qlen 2, G 4: 8 rows
     ("fp16", 2, 3, 8, 4, 64, 16, [77, 3]),          # 6 rows -> R 8 with 2 idle rows
     ("bf16", 2, 4, 16, 4, 128, 32, [200, 64]),      # 16 rows: one 16-row block
-    ("fp16", 1, 8, 8, 1, 128, 16, [300]),           # MQA, 64 rows: two 32-row blocks
+    ("fp16", 1, 8, 8, 1, 128, 16, [300]),           # MQA, 64 rows: one 64-row block
     ("bf16", 5, 1, 8, 8, 128, 16, [1, 2, 3, 16, 17]),  # MHA
     ("fp16", 2, 1, 24, 3, 64, 48, [500, 1000]),     # G 8, page 48
 ]
