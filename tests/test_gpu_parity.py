@@ -158,6 +158,35 @@ def test_smallq_mha_fp16(kv_len):
     print("  planner S=%d" % plan.num_splits, flush=True)
 
 
+DENSE_ROWS = [
+    # dtype, Hq, Hkv, q_len, kv_len, d: packed rows G * q_len per unit
+    ("bf16", 8, 8, 40, 700, 128),    # MHA, 40 rows: a 64-row block (Q staged in LDS)
+    ("fp16", 16, 2, 8, 1500, 128),   # GQA 8, 64 rows
+    ("bf16", 4, 1, 24, 300, 64),     # MQA, 96 rows: two 64-row blocks at d 64
+    ("fp16", 8, 4, 12, 999, 128),    # GQA 2, 24 rows: one 32-row block
+]
+
+
+@pytest.mark.parametrize("spec", DENSE_ROWS, ids=lambda s: "%s-G%d-q%d-d%d" % (
+    s[0], s[1] // s[2], s[3], s[5]))
+@pytest.mark.parametrize("S", [0, 1, 4])
+def test_dense_many_rows(spec, S):
+    """The dense small-query path with units of more than 16 rows (32- and
+    64-row workgroups)."""
+    dt, hq, hkv, qlen, kvlen, d = spec
+    wl = W.make_dense(2100 + qlen + d, dt, hq, hkv, qlen, kvlen, d)
+    case("dense %s Hq%d/Hkv%d q%d kvLen %d d%d S=%d" % (dt, hq, hkv, qlen, kvlen, d, S))
+    ref_o, ref_l = oracle.dense_attention(wl.q, wl.k, wl.v, dt, scale=wl.scale)
+    out, lse = api.dense_fwd(to_dev(wl.q, dt), to_dev(wl.k, dt), to_dev(wl.v, dt), num_splits=S,
+                             softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    check_out(bits_of(out), ref_o, dt)
+    check_lse(lse.cpu().numpy(), ref_l)
+    print("  plan S=%d rows/blk=%d grid=%d" % (api.last_plan().num_splits,
+                                               api.last_plan().rows_per_block,
+                                               api.last_plan().grid), flush=True)
+
+
 # ---------------------------------------------------------- any head_dim ----
 
 ODD_DIMS = [1, 7, 16, 24, 33, 48, 80, 96, 100, 112, 130, 160, 192, 200, 255, 256, 32]
