@@ -11,14 +11,15 @@
 //       v_mfma_f32_16x16x32_{bf16,f16}, D/32 instructions per 16-key tile.
 //       With K as the A operand, lane l holds the scores of query row l%16
 //       for keys 4*(l/16)..+3: one row per lane, so the softmax needs no
-//       per-key lane reductions, and the probabilities, rounded to the
-//       16-bit type, are already the A operand of the next product.
+//       per-key lane reductions, and the probabilities are already in the
+//       A layout of the next product.
 //   O (16 rows x D) += P (16 x 16 keys) . V (16 keys x D)
-//       v_mfma_f32_16x16x16_{bf16,f16}, D/16 instructions per tile, plus one
-//       more with an all-ones B operand whose output column is the running
-//       sum of the rounded probabilities: O is divided by exactly the
-//       weights it was built from.  The LSE uses a float32 running sum of
-//       the unrounded probabilities.
+//       v_mfma_f32_16x16x32_{bf16,f16}, D/16 instructions per tile: a
+//       lane's 8 k-values are its 4 keys' probabilities rounded to the
+//       16-bit type and the 4 rounded residues (A), against its 4 V values
+//       twice (B), so P carries 16 (bf16) or 22 (fp16) significant bits.
+//       O and the LSE are normalised by a float32 running sum of the
+//       unrounded probabilities.
 //       The V tile sits in the wave's LDS slot and is read back with
 //       ds_read_b64_tr_b16, which delivers the key-major B operand.
 //
@@ -61,7 +62,6 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef short s4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
@@ -75,10 +75,6 @@ struct Mf<1> {  // bfloat16
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a),
                                                    __builtin_bit_cast(bf8_t, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ f4_t pv(uint2 a, uint2 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a),
-                                                     __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
-  }
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, bf2_t));
   }
@@ -89,7 +85,6 @@ struct Mf<1> {  // bfloat16
   static __device__ __forceinline__ f2_t widen(uint32_t v) {
     return (f2_t){__builtin_bit_cast(float, v << 16), __builtin_bit_cast(float, v & 0xFFFF0000u)};
   }
-  static constexpr uint32_t kOnePair = 0x3F803F80u;
 };
 
 template <>
@@ -97,10 +92,6 @@ struct Mf<0> {  // IEEE binary16
   static __device__ __forceinline__ f4_t qk(uint4 a, uint4 b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
                                                   __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f4_t pv(uint2 a, uint2 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a),
-                                                 __builtin_bit_cast(h4_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, h2_t));
@@ -111,7 +102,6 @@ struct Mf<0> {  // IEEE binary16
   static __device__ __forceinline__ f2_t widen(uint32_t v) {
     return __builtin_convertvector(__builtin_bit_cast(h2_t, v), f2_t);
   }
-  static constexpr uint32_t kOnePair = 0x3C003C00u;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -371,13 +361,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     }
   }
 
-  f4_t acc[NRB][DB + 1];  // O blocks; acc[r][DB] is the all-ones block: column sums = l
+  f4_t acc[NRB][DB];  // O blocks
   float m[NRB];           // reference max of row n16 of block r (S^T layout), log2 units
   float l32[NRB];         // float32 sum of this lane's probabilities (row n16)
 #pragma unroll
   for (int r = 0; r < NRB; ++r) {
 #pragma unroll
-    for (int db = 0; db <= DB; ++db) acc[r][db] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DB; ++db) acc[r][db] = (f4_t){0.f, 0.f, 0.f, 0.f};
     m[r] = -INFINITY;
     l32[r] = 0.f;
   }
@@ -456,13 +446,12 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   // A 16-bit probability rounded once has a relative error up to 2^-9
   // (bfloat16) or 2^-12 (fp16); times large, cancelling V rows that can
   // exceed the output tolerance (seen at 0.06 in bf16 and 0.015 in fp16
-  // with 8x outlier K/V rows).  So P goes in as the rounded value plus the
-  // rounding of its residue (16 or 22 significant bits together), for P.V
-  // and for the row sums, in one 16x16x32 product per block: a lane's 8
-  // k-values are its 4 keys' rounded P and their 4 residues (A), against
-  // its 4 V values twice (B).  Same key order as the 16x16x16 layout, so no
-  // lane exchange.
-  constexpr bool kSplitP = true;
+  // with 8x outlier K/V rows).  So P goes into P.V as the rounded value plus
+  // the rounding of its residue (16 or 22 significant bits together), in
+  // one 16x16x32 product per d block: a lane's 8 k-values are its 4 keys'
+  // rounded P and their 4 residues (A), against its 4 V values twice (B).
+  // The keys keep the order of the score layout, so no lane exchange.  The
+  // row sums then come from the float32 sum of the unrounded P.
   // Scores, online softmax and P.V of one tile: kq holds this lane's K
   // operand chunks, vop(db) returns the V operand of d block db.
   auto tile_math = [&](const uint4 (&kq)[KB], auto vop, int tt) {
@@ -500,7 +489,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
         for (int i = 0; i < 4; ++i) {
           const float ai = from_lane(alpha, 4 * g + i);  // O rows 4g+i live in lanes of row 4g+i
 #pragma unroll
-          for (int db = 0; db <= DB; ++db) acc[r][db][i] *= ai;
+          for (int db = 0; db < DB; ++db) acc[r][db][i] *= ai;
         }
       }
       float pr[4];
@@ -511,36 +500,18 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       }
       l32[r] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       pa[r] = make_uint2(M::pack(pr[0], pr[1]), M::pack(pr[2], pr[3]));
-      if constexpr (kSplitP) {  // the rounding residue, as a second operand
-        const f2_t h01 = M::widen(pa[r].x), h23 = M::widen(pa[r].y);
-        pl[r] = make_uint2(M::pack(pr[0] - h01[0], pr[1] - h01[1]),
-                           M::pack(pr[2] - h23[0], pr[3] - h23[1]));
-      }
+      const f2_t h01 = M::widen(pa[r].x), h23 = M::widen(pa[r].y);  // the rounding residue
+      pl[r] = make_uint2(M::pack(pr[0] - h01[0], pr[1] - h01[1]),
+                         M::pack(pr[2] - h23[0], pr[3] - h23[1]));
     }
-    // O += P . V for each row block (one V operand per d block), and the
-    // all-ones block for l
+    // O += P . V for each row block (one V operand per d block)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const uint2 vt = vop(db);
 #pragma unroll
-      for (int r = 0; r < NRB; ++r) {
-        if constexpr (kSplitP) {
-          acc[r][db] = M::qk(make_uint4(pa[r].x, pa[r].y, pl[r].x, pl[r].y),
-                             make_uint4(vt.x, vt.y, vt.x, vt.y), acc[r][db]);
-        } else {
-          acc[r][db] = M::pv(pa[r], vt, acc[r][db]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-      if constexpr (kSplitP) {
-        acc[r][DB] = M::qk(make_uint4(pa[r].x, pa[r].y, pl[r].x, pl[r].y),
-                           make_uint4(M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair),
-                           acc[r][DB]);
-      } else {
-        acc[r][DB] = M::pv(pa[r], make_uint2(M::kOnePair, M::kOnePair), acc[r][DB]);
-      }
+      for (int r = 0; r < NRB; ++r)
+        acc[r][db] = M::qk(make_uint4(pa[r].x, pa[r].y, pl[r].x, pl[r].y),
+                           make_uint4(vt.x, vt.y, vt.x, vt.y), acc[r][db]);
     }
   };
   // transposed read of d block db of the wave's staged V tile
@@ -642,13 +613,12 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       make_rsrc(p.lse_part, uint32_t(min<long>((long)p.num_splits * p.nrows * 4, 0xFFFFFFFFl)));
 
   // ---- merge the waves through LDS and write, one 16-row block at a time --
-  // O layout: lane l holds rows 4g..4g+3, columns 16db + n16; l is acc[DB].
-  // m of row r is held by lanes with n16 == r.
+  // O layout: lane l holds rows 4g..4g+3, columns 16db + n16.  m and the
+  // probability sum of row r are held by lanes with n16 == r.
   constexpr int RMAX = 16;
   float* s_acc = reinterpret_cast<float*>(s_buf);  // [NW][16][D]
   __shared__ float s_m[NW][RMAX];
-  __shared__ float s_l[NW][RMAX];    // sums of the rounded probabilities (normalise O)
-  __shared__ float s_l32[NW][RMAX];  // float32 sums (LSE)
+  __shared__ float s_l32[NW][RMAX];  // float32 probability sums
 #pragma unroll
   for (int blk = 0; blk < NRB; ++blk) {
     const int rows_here = min(RMAX, rows_b - row0 - 16 * blk);
@@ -662,7 +632,6 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           s_acc[((long)wave * RMAX + r) * D + db * 16 + n16] = acc[blk][db][i];
-        if (n16 == 0) s_l[wave][r] = acc[blk][DB][i];
       }
     }
     if (g == 0 && n16 < rows_here) {
@@ -678,18 +647,17 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       float Mx = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][r]);
-      float num = 0.f, den = 0.f, den32 = 0.f;
+      float num = 0.f, den = 0.f;
       if (Mx != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const float f = (s_m[w][r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - Mx);
           num = fmaf(f, s_acc[((long)w * RMAX + r) * D + d], num);
-          den = fmaf(f, s_l[w][r], den);
-          den32 = fmaf(f, s_l32[w][r], den32);
+          den = fmaf(f, s_l32[w][r], den);
         }
       }
       const float o = (Mx == -INFINITY) ? 0.f : num / den;
-      const float lse = (Mx == -INFINITY) ? -INFINITY : (Mx + log2f(den32)) * kLn2;
+      const float lse = (Mx == -INFINITY) ? -INFINITY : (Mx + log2f(den)) * kLn2;
       const int i = pr / p.heads_per_unit;
       const int hq = hq0 + pr % p.heads_per_unit;
       const long nrow = row_of(i, hq);
