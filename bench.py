@@ -11,6 +11,10 @@ not in the 256 MiB last-level cache from the previous step.
 value = algorithmic KV bytes per step (valid keys x Hkv x d x 2 x 2 B)
         / wall time per step, in GB/s.
 
+Beside it: the roofline of the split kernel, the spread of single launches,
+the read-only probes over the same bytes (the empirical ceiling), and the
+float64 oracle timed on the host cores.
+
 Prints one JSON line (see --help for options).
 """
 import argparse
@@ -42,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the read-only probes (stream and page-gather reads of the "
+                         "same KV bytes) that give the empirical ceiling")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy this many MiB device to device once (the "
                          "known-size copy that scales the HBM byte counters)")
@@ -150,6 +157,11 @@ def main():
     def pct(q):
         return round(one[min(n_one - 1, int(q * (n_one - 1) + 0.5))], 3)
 
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = read_ceiling(wl, pools, None if dense else (bt, sl),
+                               last.split_keys if last.num_splits > 1 else 0, K, stream)
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -212,9 +224,60 @@ def main():
         "single_launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "n": n_one,
                              "method": "event pair around each launch, host-paced"},
     }
+    if ceiling is not None:
+        ceiling["kernel_over_best_probe"] = round(
+            achieved / max(v["GB/s"] for k, v in ceiling.items() if isinstance(v, dict)), 4)
+        rec["read_ceiling"] = ceiling
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
+
+
+def read_ceiling(wl, pools, paged, split_keys, steps, stream):
+    """The empirical ceiling: read-only probes (libattn_probe.so) over the
+    same KV bytes and pools as the timed calls, timed the same way (two
+    events around `steps` back-to-back launches, pools rotated).
+      stream_read       the first half of the KV bytes from each pool's K
+                        tensor and the second half from its V tensor,
+                        contiguous, 512 workgroups
+      page_gather_read  (paged) the valid keys' K and V rows, walked as the
+                        decode kernel walks them (split as the timed calls
+                        were), with no arithmetic"""
+    import torch
+    from split_kv_paged_amd import probe
+
+    def timed(calls):
+        for i in range(3):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            calls[i % len(calls)]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def entry(nbytes, us):
+        gbs = nbytes / us / 1e3
+        return {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "us": round(us, 3)}
+
+    half = wl.kv_bytes // 2 // 16 * 16
+    sums = torch.empty(512, dtype=torch.int32, device=pools[0][0].device)
+    calls = [probe.prepared_stream_read(k, v, half, half, 512, sums, stream)[0] for k, v in pools]
+    res = {"stream_read": entry(2 * half, timed(calls))}
+    if paged is not None:
+        bt, sl = paged
+        first, psums = probe.prepared_page_read(pools[0][0], pools[0][1], bt, sl,
+                                                wl.max_seqlen_k, split_keys, None, stream)
+        calls = [first] + [probe.prepared_page_read(k, v, bt, sl, wl.max_seqlen_k, split_keys,
+                                                    psums, stream)[0] for k, v in pools[1:]]
+        res["page_gather_read"] = entry(wl.kv_bytes, timed(calls))
+        res["page_gather_read"]["split_keys"] = split_keys
+    res["method"] = "read-only probes over the same KV bytes and pools, events around %d " \
+                    "back-to-back launches" % steps
+    return res
 
 
 def measured_traffic(workload, num_splits):

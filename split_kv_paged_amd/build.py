@@ -1,4 +1,6 @@
-"""Build libattn_decode.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build libattn_decode.so (the C-ABI library) and libattn_probe.so (the
+read-only bandwidth probes of include/attn_probe.h) in-tree with hipcc for
+gfx950.
 
 Every translation unit is compiled with hipcc; the shared object is linked
 against the HIP runtime that torch loads (``torch/lib/libamdhip64.so``) so a
@@ -20,6 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+PROBE_DIR = os.path.join(PKG, "probe")
+PROBE_LIB_PATH = os.path.join(PKG, "libattn_probe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
@@ -52,36 +56,46 @@ def _run(cmd, verbose):
 
 
 def sources():
+    """Sources of libattn_decode.so."""
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def probe_sources():
+    """Sources of libattn_probe.so."""
+    return sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip")))
+
+
 def build(verbose=False, jobs=None):
-    """Compile every source and link the library.  Always rebuilds."""
+    """Compile every source and link both libraries.  Always rebuilds."""
     hipcc = os.path.join(ROCM, "bin", "hipcc")
     if not os.path.exists(hipcc):
         hipcc = shutil.which("hipcc") or hipcc
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    targets = [(LIB_PATH, sources()), (PROBE_LIB_PATH, probe_sources())]
+    objs = {}
     procs = []
-    for src in sources():
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
-        if src.endswith(".cpp"):
-            cmd[1:1] = ["-x", "hip"]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((subprocess.Popen(cmd), src))
-        objs.append(obj)
+    for lib_path, srcs in targets:
+        objs[lib_path] = []
+        for src in srcs:
+            obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+            cmd = [hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+            if src.endswith(".cpp"):
+                cmd[1:1] = ["-x", "hip"]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((subprocess.Popen(cmd), src))
+            objs[lib_path].append(obj)
     failed = [s for p, s in procs if p.wait() != 0]
     if failed:
         raise RuntimeError("hipcc failed on: " + ", ".join(failed))
     rt = _hip_runtime_dir()
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    link = ["g++", "-shared", "-o", tmp] + objs + [
-        "-L" + rt, "-l:libamdhip64.so", "-Wl,-rpath," + rt, "-Wl,-rpath," + os.path.join(ROCM, "lib"),
-        "-Wl,--no-undefined", "-lpthread"]
-    _run(link, verbose)
-    os.replace(tmp, LIB_PATH)
+    for lib_path, _ in targets:
+        tmp = lib_path + ".tmp%d" % os.getpid()
+        link = ["g++", "-shared", "-o", tmp] + objs[lib_path] + [
+            "-L" + rt, "-l:libamdhip64.so", "-Wl,-rpath," + rt,
+            "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-Wl,--no-undefined", "-lpthread"]
+        _run(link, verbose)
+        os.replace(tmp, lib_path)
     return LIB_PATH
 
 
