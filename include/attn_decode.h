@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum {
     ATTN_OK = 0,
@@ -94,9 +94,12 @@ typedef struct {
                             * the mean length) whose longest sequence exceeds
                             * two compute units' fair shares of all keys,
                             * into pieces of at most half a share (an
-                            * addition to the pages' rule).  0 <= sum <=
-                            * batch * max_seqlen_k, else ATTN_ERR_SHAPE; a
-                            * wrong but in-range value changes only speed. */
+                            * addition to the pages' rule), and a split call
+                            * may launch the compact list (see
+                            * attn_plan.extra_blocks) instead of every
+                            * (unit, split) pair.  0 <= sum <= batch *
+                            * max_seqlen_k, else ATTN_ERR_SHAPE; a wrong but
+                            * in-range value changes only speed. */
 } attn_decode_shape;
 
 /* Dense small-query problem (the SmallQ README's [heads, qLen, headDim]
@@ -126,7 +129,8 @@ typedef struct {
                              /* rows and 64 beyond (KV read once per block)    */
     int32_t row_blocks;      /* ceil(rows_per_unit / rows_per_block)           */
     int32_t units;           /* batch * head units * row_blocks               */
-    int32_t grid;            /* workgroups of the split kernel = units * S    */
+    int32_t grid;            /* workgroups of the split kernel: units * S, or */
+                             /* units + extra_blocks with the compact list    */
     int32_t split_granule;   /* split lengths are multiples of this many keys  */
     int32_t num_cus;         /* compute units the plan was made for           */
     int32_t combine;         /* how S > 1 partials are merged: 0 none (S = 1), */
@@ -138,6 +142,18 @@ typedef struct {
                              /* paged + tile head dim (32, 64, 128 or 256)     */
     int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
+    int32_t extra_blocks;    /* 0: the grid is split-major, every (unit,      */
+                             /* split) pair has a workgroup (empty splits     */
+                             /* return at once).  > 0 (paged, S > 1, length   */
+                             /* sum given, batch <= 1024, and a smaller grid): */
+                             /* a compact list: extra_blocks workgroups take  */
+                             /* the splits 1.. of the sequences that need     */
+                             /* them (listed on the device from the lengths), */
+                             /* then one workgroup per unit runs split 0.     */
+                             /* extra_blocks = max(1, floor(sum_seqlen_k / C) */
+                             /* x head units x row_blocks), enough for one    */
+                             /* item each when the sum is right; with a wrong */
+                             /* sum they loop over the items (same results).  */
     int64_t workspace_bytes; /* bytes of workspace the forward call needs     */
 } attn_plan;
 

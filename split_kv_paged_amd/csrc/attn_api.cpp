@@ -140,13 +140,26 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   const int64_t row_blocks = ceil_div(rows_per_unit, rpb);
   const int64_t unit_heads = pack ? hkv : hq;
   const int64_t units = batch * unit_heads * row_blocks;
-  const int64_t grid = units * splits;
+  int64_t grid = units * splits;
   if (grid > INT32_MAX || rows_per_unit > INT32_MAX) return ATTN_ERR_SHAPE;
   const int64_t nrows = batch * q_len * int64_t(hq);
   // one split length for the batch: whole 16-key granules, S of them cover max_seqlen_k
   const int64_t split_keys =
       int64_t(kGranule) * std::max<int64_t>(1, ceil_div(ceil_div(max_seqlen_k, kGranule), splits));
   if (split_keys > INT32_MAX) return ATTN_ERR_SHAPE;
+  // Compact list (paged splits with a length sum): sequence b needs
+  // ceil(L_b / C) - 1 <= floor(L_b / C) splits past the first, and the sum
+  // of floors is at most floor(sum / C), so that many extra workgroups per
+  // head unit and row block give every extra split one workgroup.  Used
+  // when it launches fewer workgroups than the split-major grid.
+  int64_t extra = 0;
+  if (!dense && splits > 1 && sum_seqlen_k > 0 && batch <= skv::kMaxOrderBatch) {
+    const int64_t bound = std::max<int64_t>(1, sum_seqlen_k / split_keys * unit_heads * row_blocks);
+    if (units + bound < grid) {
+      extra = bound;
+      grid = units + extra;
+    }
+  }
   int64_t ws = 0;
   if (splits > 1) {
     // the fused combine addresses the partials with 32-bit byte offsets
@@ -168,6 +181,7 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   out->combine = splits > 1 ? 2 : 0;
   out->kernel = kernel_id(head_dim, !dense);
   out->split_keys = int(split_keys);
+  out->extra_blocks = int(extra);
   out->workspace_bytes = ws;
   return ATTN_OK;
 }
@@ -248,6 +262,7 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   // Paged calls whose grid needs more than one round run the first split's
   // sequences longest first (ranked inside its workgroups).
   prm.by_length = paged && prm.batch <= skv::kMaxOrderBatch && plan.grid > plan.num_cus;
+  prm.extra_blocks = paged ? plan.extra_blocks : 0;
   if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   g_last_plan = plan;

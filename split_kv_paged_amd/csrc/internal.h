@@ -40,6 +40,10 @@ struct SplitParams {
   int n_si, n_sh;
   float scale_log2;    // softmax scale * log2(e)
   int by_length;       // paged: run sequences longest first (batch <= kMaxOrderBatch)
+  int extra_blocks;    // paged, 0: split-major grid of units * num_splits workgroups;
+                       // > 0: extra_blocks workgroups take the splits >= 1 from a
+                       // device-built list, then one workgroup per unit runs split 0
+                       // (batch <= kMaxOrderBatch)
   int seq_add;         // paged: keys attended = seqlens[b] + seq_add (appended keys)
   int causal;          // query i of q_len sees keys j <= L - q_len + i
   const int32_t* cu_q; // varlen: queries of sequence b are rows cu_q[b] .. cu_q[b+1]-1

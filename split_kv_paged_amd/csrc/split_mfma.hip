@@ -171,7 +171,8 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
 // NRB: 16-row blocks a workgroup carries (1; 2 or 4 when a unit has more
 // than 16 or 32 packed rows, so its KV is read once for up to 64 rows).
 template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB>
-__global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
+__device__ __forceinline__ void split_unit(const SplitParams& p, const int split, const int b,
+                                           const int uh, const int rb, const int tid) {
   using M = Mf<DT>;
   constexpr int KB = D / 32;        // 16x16x32 products per tile (QK)
   constexpr int DB = D / 16;        // 16x16x16 products per tile (PV)
@@ -199,55 +200,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     uint4 v[KB];
   };
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15;  // S^T: query row; O: column within a 16-wide d block
   const int g = lane >> 4;    // S^T: key group (keys 4g..4g+3); O: rows 4g..4g+3
 
-  // Workgroups run split-major from the last split down: the last splits
-  // exist only for the longest sequences, so their work is dispatched first
-  // and the short remainder fills in behind it.
-  // When the grid takes more than one round of workgroups, the first split
-  // (the one every sequence has) also runs its sequences longest first (a
-  // longest-processing-time order): each of its workgroups ranks the batch
-  // by length, ties by index.  The later splits, mostly empty, skip that.
-  // Within a split, the row blocks of one (sequence, head unit) sit 8
-  // workgroups apart: workgroups are dealt to the 8 XCDs round-robin, so
-  // they land on the same XCD, close in time, and the second one to read
-  // a KV tile finds it in that XCD's L2.  Head units go in groups of 8:
-  // workgroup g*8*row_blocks + rb*n + i runs head unit 8g + i, row block
-  // rb, where n = 8 except in the last, shorter group.
-  const int units = p.batch * p.unit_heads * p.row_blocks;
-  const int split = p.num_splits - 1 - int(blockIdx.x) / units;
-  int rb, bid;
-  {
-    const int pairs = p.batch * p.unit_heads;
-    const int id = int(blockIdx.x) % units;
-    const int grp = id / (8 * p.row_blocks);
-    const int rem = id - grp * 8 * p.row_blocks;
-    const int n = min(8, pairs - grp * 8);
-    rb = rem / n;
-    bid = grp * 8 + rem % n;
-  }
-  const int uh = bid % p.unit_heads;
-  int b = bid / p.unit_heads;
-  if (PAGED && p.by_length && split == 0) {
-    __shared__ int s_len[kMaxOrderBatch];
-    __shared__ int s_seq;
-    for (int i = threadIdx.x; i < p.batch; i += NW * 64) s_len[i] = p.seqlens[i];
-    __syncthreads();
-    for (int i = threadIdx.x; i < p.batch; i += NW * 64) {
-      const int li = s_len[i];
-      int rank = 0;
-      for (int j = 0; j < p.batch; ++j) {
-        const int lj = s_len[j];
-        rank += (lj > li) || (lj == li && j < i);
-      }
-      if (rank == b) s_seq = i;
-    }
-    __syncthreads();
-    b = s_seq;
-  }
   const int hq0 = uh * p.heads_per_unit;
   const int h = hq0 / p.group;
 
@@ -314,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   __shared__ __attribute__((aligned(16))) uint8_t s_q[kQLds ? 16 * NRB * D * 2 : 16];
   if constexpr (kQLds) {
     constexpr int kChunks = 16 * NRB * (D / 8);  // 16-byte chunks of the 64 rows
-    for (int ci = threadIdx.x; ci < kChunks; ci += NW * 64) {
+    for (int ci = tid; ci < kChunks; ci += NW * 64) {
       const int rr = ci / (D / 8), cc = ci % (D / 8);
       const int rowq = row0 + rr;
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -640,7 +597,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     }
     __syncthreads();
 
-    for (int t = threadIdx.x; t < rows_here * hd; t += NW * 64) {
+    for (int t = tid; t < rows_here * hd; t += NW * 64) {
       const int r = t / hd;
       const int d = t % hd;
       const int pr = row0 + 16 * blk + r;
@@ -688,14 +645,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
   __syncthreads();
   const int unit = (b * p.unit_heads + uh) * p.row_blocks + rb;
-  if (threadIdx.x == 0)
+  if (tid == 0)
     s_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_SYSTEM) == nsplit - 1;
   __syncthreads();
   if (!s_last) return;
   const int S = nsplit;
   const int rows_unit = min(16 * NRB, rows_b - row0);
-  for (int t = threadIdx.x; t < rows_unit * hd; t += NW * 64) {
+  for (int t = tid; t < rows_unit * hd; t += NW * 64) {
     const int r = t / hd;
     const int d = t % hd;
     const int pr = row0 + r;
@@ -733,8 +690,125 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     if (d == 0 && p.lse)
       p.lse[lse_of(i, hq)] = mx == -INFINITY ? -INFINITY : (mx + log2f(wsum)) * kLn2;
   }
-  if (threadIdx.x == 0)
+  if (tid == 0)
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Work lists.
+// Split-major (extra_blocks == 0): workgroups run split-major from the last
+// split down.  The last splits exist only for the longest sequences, so
+// their work is dispatched first and the short remainder fills in behind
+// it; a split past a sequence's last key returns at once.
+// Compact (extra_blocks > 0, a ragged batch whose length sum the caller
+// gave): the first extra_blocks workgroups take the splits 1 .. n_b - 1 of
+// the sequences that need them, from a list each of them builds from the
+// lengths; then one workgroup per unit runs split 0.  The empty splits of
+// short sequences are never launched.  The host sizes extra_blocks from the
+// length sum so that each takes one item; with a smaller count (a wrong
+// sum) they loop over the items, which stays correct.
+// In both, when the grid takes more than one round of workgroups, split 0
+// (the one every sequence has) runs its sequences longest first (a
+// longest-processing-time order): each of its workgroups ranks the batch
+// by length, ties by index.
+// The row blocks of one (sequence, head unit) sit 8 workgroups apart:
+// workgroups are dealt to the 8 XCDs round-robin, so they land on the same
+// XCD, close in time, and the second one to read a KV tile finds it in
+// that XCD's L2.  Head units go in groups of 8: workgroup g*8*row_blocks +
+// rb*n + i runs head unit 8g + i, row block rb, where n = 8 except in the
+// last, shorter group.
+// EXTRA: a kernel built for the compact list (its loop over items costs
+// about ten VGPRs, so the split-major kernels are built without it).
+template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB, bool EXTRA>
+__global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
+  static_assert(PAGED || !EXTRA, "the compact list is for paged calls");
+  __shared__ int s_seq[kMaxOrderBatch + 1];
+  if (EXTRA && int(blockIdx.x) < p.extra_blocks) {
+    // Extra items of sequence b: (n_b - 1) x head units x row blocks, with
+    // n_b = ceil(L_b / split_keys) splits (at most num_splits, as in the
+    // split-major grid).  s_seq[b] = items of sequences before b (an
+    // exclusive prefix); s_seq[batch] = all items.
+    const int per_seq = p.unit_heads * p.row_blocks;
+    for (int i = threadIdx.x; i < p.batch; i += NW * 64) {
+      const int L = p.seqlens[i] + p.seq_add;
+      const int more = L > p.split_keys ? (L - 1) / p.split_keys : 0;
+      s_seq[i + 1] = min(more, p.num_splits - 1) * per_seq;
+    }
+    if (threadIdx.x == 0) s_seq[0] = 0;
+    __syncthreads();
+    if (threadIdx.x < 64) {  // wave 0 scans s_seq[1 .. batch] in place, 64 chunks
+      const int lane = threadIdx.x;
+      const int chunk = (p.batch + 63) / 64;
+      const int lo = 1 + min(p.batch, lane * chunk);
+      const int hi = 1 + min(p.batch, (lane + 1) * chunk);
+      int run = 0;
+      for (int i = lo; i < hi; ++i) run += s_seq[i];
+      int incl = run;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      run = incl - run;
+      for (int i = lo; i < hi; ++i) {
+        run += s_seq[i];
+        s_seq[i] = run;
+      }
+    }
+    __syncthreads();
+    const int total = s_seq[p.batch];
+    for (int item = int(blockIdx.x); item < total; item += p.extra_blocks) {
+      int lo = 0, hi = p.batch;  // s_seq[lo] <= item < s_seq[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_seq[mid] <= item) lo = mid; else hi = mid;
+      }
+      // every lane found the same values: keep them scalar
+      const int bs = __builtin_amdgcn_readfirstlane(lo);
+      const int r = __builtin_amdgcn_readfirstlane(item - s_seq[lo]);
+      const int rem = r % per_seq;
+      // The thread index passes through an empty asm, so that nothing the
+      // unit derives from it is hoisted out of this loop and kept live
+      // across it (that raised the kernel's VGPR count by a third).
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      split_unit<DT, D, NW, NBUF, PAGED, GEN, NRB>(p, 1 + r / per_seq, bs, rem % p.unit_heads,
+                                                  rem / p.unit_heads, tid);
+      __syncthreads();  // the unit's LDS is reused by the next one
+    }
+    return;
+  }
+  const int units = p.batch * p.unit_heads * p.row_blocks;
+  const int id0 = int(blockIdx.x) - (EXTRA ? p.extra_blocks : 0);
+  const int split = EXTRA ? 0 : p.num_splits - 1 - id0 / units;
+  int rb, bid;
+  {
+    const int pairs = p.batch * p.unit_heads;
+    const int id = id0 % units;
+    const int grp = id / (8 * p.row_blocks);
+    const int rem = id - grp * 8 * p.row_blocks;
+    const int n = min(8, pairs - grp * 8);
+    rb = rem / n;
+    bid = grp * 8 + rem % n;
+  }
+  const int uh = bid % p.unit_heads;
+  int b = bid / p.unit_heads;
+  if (PAGED && p.by_length && split == 0) {
+    int* const s_len = s_seq;
+    __shared__ int s_pick;
+    for (int i = threadIdx.x; i < p.batch; i += NW * 64) s_len[i] = p.seqlens[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < p.batch; i += NW * 64) {
+      const int li = s_len[i];
+      int rank = 0;
+      for (int j = 0; j < p.batch; ++j) {
+        const int lj = s_len[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+      if (rank == b) s_pick = i;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(s_pick);
+  }
+  split_unit<DT, D, NW, NBUF, PAGED, GEN, NRB>(p, split, b, uh, rb, threadIdx.x);
 }
 
 // Waves per workgroup: 8 up to D = 128, 4 at D = 256 (accumulators and
@@ -750,7 +824,15 @@ hipError_t launch_mfma_k(const SplitParams& p, int grid, hipStream_t s) {
   constexpr bool kDirect = GEN != 2 && D >= 64;
   constexpr int NW = D <= 128 ? 8 : 4;
   constexpr int NBUF = kDirect ? 0 : D >= 128 ? 1 : 2;
-  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB>), dim3(grid),
+  if (p.extra_blocks > 0) {
+    if constexpr (PAGED) {
+      hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true>), dim3(grid),
+                         dim3(NW * 64), 0, s, p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false>), dim3(grid),
                      dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }

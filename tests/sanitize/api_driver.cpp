@@ -43,7 +43,11 @@ static bool valid_status(attn_status s) { return s >= ATTN_OK && s <= ATTN_ERR_D
 
 static void check_plan(const attn_plan& p, int64_t max_seqlen) {
   CHECK(p.num_splits >= 1 && p.num_splits <= 1024, "plan splits in range");
-  CHECK(int64_t(p.grid) == int64_t(p.units) * p.num_splits, "grid = units * splits");
+  CHECK(int64_t(p.grid) == (p.extra_blocks > 0 ? int64_t(p.units) + p.extra_blocks
+                                                : int64_t(p.units) * p.num_splits),
+        "grid = units * splits, or units + extra blocks");
+  CHECK(p.extra_blocks == 0 || (p.num_splits > 1 && p.grid < int64_t(p.units) * p.num_splits),
+        "a compact list only for a split call, and only when it is smaller");
   CHECK(p.split_keys >= 16 && p.split_keys % 16 == 0, "split keys in granules");
   CHECK(int64_t(p.split_keys) * p.num_splits >= max_seqlen, "splits cover max_seqlen_k");
   CHECK(p.workspace_bytes >= 0, "workspace size");

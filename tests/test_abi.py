@@ -298,6 +298,41 @@ def test_ragged_hint_plan(lib, name, kw, want):
     assert plan.num_splits >= plan0.num_splits
 
 
+# Compact list: extra_blocks = max(1, floor(sum / C) * head units * row
+# blocks), used when units + extra_blocks < units * S.  Worked by hand:
+#   ragged d64:  C = 16 * ceil(486 / 5) = 1568; floor(112861 / 1568) = 71;
+#                71 * 8 = 568; 1024 + 568 = 1592 < 5120
+#   ragged d128: C = 16 * ceil(416 / 11) = 608; floor(40957 / 608) = 67;
+#                67 * 8 = 536; 256 + 536 = 792 < 2816
+#   long uniform: C = 1184; floor(65536 / 1184) * 4 = 220; 16 + 220 = 236 is
+#                not below 16 * 14 = 224: split-major
+#   cap:         C = 512; floor(65791 / 512) = 128; 256 + 128 < 32768
+#   ragged 32 rows: as ragged d128 (one 32-row block per unit)
+COMPACT_EXTRA = {"ragged d64": 568, "ragged d128": 536, "uniform ~1000": 0, "long uniform": 0,
+                 "ragged under two shares": 0, "cap": 128, "ragged 32 rows": 536}
+
+
+@pytest.mark.parametrize("name,kw,want", RAGGED_CASES, ids=[c[0] for c in RAGGED_CASES])
+def test_compact_list_plan(lib, name, kw, want):
+    code, plan = _plan(lib, **kw)
+    assert L.STATUS[code] == "ATTN_OK"
+    assert plan.extra_blocks == COMPACT_EXTRA[name]
+    if plan.extra_blocks:
+        assert plan.grid == plan.units + plan.extra_blocks < plan.units * plan.num_splits
+    else:
+        assert plan.grid == plan.units * plan.num_splits
+    # the compact list changes the grid only: same splits, same workspace
+    code0, plan0 = _plan(lib, **dict(kw, sum_L=0, S=plan.num_splits))
+    assert plan0.extra_blocks == 0 and plan0.grid == plan0.units * plan0.num_splits
+    assert plan0.workspace_bytes == plan.workspace_bytes
+    assert plan0.split_keys == plan.split_keys
+    # a batch over 1024 sequences keeps the split-major grid
+    if plan.num_splits > 1:
+        big = dict(kw, batch=1100, sum_L=kw["sum_L"] * 1100 // kw["batch"], S=plan.num_splits)
+        code2, plan2 = _plan(lib, **big)
+        assert L.STATUS[code2] == "ATTN_OK" and plan2.extra_blocks == 0
+
+
 def test_ragged_hint_rejects_out_of_range(lib):
     base = dict(batch=4, q_len=1, hq=8, hkv=2, maxp=64, max_L=1000)
     assert L.STATUS[_plan(lib, **base, sum_L=-1)[0]] == "ATTN_ERR_SHAPE"

@@ -374,6 +374,75 @@ def test_large_batches(B):
         assert_paged(wl, num_splits=S, ref=ref)
 
 
+# ------------------------------------------------------ compact split list --
+
+COMPACT = [
+    # dtype, B, q_len, Hq, Hkv, d, lengths, S, causal, new_len
+    ("fp16", 12, 1, 16, 8, 64, [8000, 1, 5, 3000, 0, 17, 1500, 2, 6000, 40, 999, 4000], 5,
+     False, 0),
+    ("bf16", 6, 8, 32, 8, 128, [3000, 10, 2500, 1, 700, 4000], 4, True, 0),  # 32-row blocks
+    ("fp16", 5, 8, 64, 8, 64, [2000, 5, 1800, 33, 900], 3, True, 0),         # 64-row blocks
+    ("bf16", 4, 4, 32, 8, 128, [1000, 13, 500, 1020], 4, True, 4),           # appended keys
+]
+
+
+@pytest.mark.parametrize("spec", COMPACT, ids=lambda c: "%s-B%d-q%d-d%d-S%d-new%d" % (
+    c[0], c[1], c[2], c[5], c[7], c[9]))
+def test_compact_split_list(spec):
+    """Given a length sum, a split call launches the extra splits from a
+    list built on the device instead of every (unit, split) pair.  With the
+    right sum each extra workgroup takes one item; with a far smaller one
+    (still in range) a single extra workgroup loops over all of them; with a
+    larger one some find nothing.  Every run matches the oracle and equals
+    the split-major run bit for bit (same splits, same merge order)."""
+    dt, B, qlen, hq, hkv, d, lens, S, causal, new_len = spec
+    if new_len:
+        wl, k_new, v_new, kc_h, vc_h = _append_case(1600 + B, dt, B, qlen, hq, hkv, d, lens,
+                                                    new_len)
+        attended = [x + new_len for x in lens]
+    else:
+        wl = W.make_paged(1600 + B, dt, B, qlen, hq, hkv, d, 16, lens, spare_pages=1)
+        kc_h, vc_h, k_new, v_new, attended = wl.k_cache, wl.v_cache, None, None, lens
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    q = to_dev(wl.q, dt)
+    kc, vc = to_dev(kc_h, dt), to_dev(vc_h, dt)
+    bt = i32_dev(wl.block_table)
+    sl = i32_dev(np.array(lens, dtype=np.int32))
+    kn = to_dev(k_new, dt) if new_len else None
+    vn = to_dev(v_new, dt) if new_len else None
+    max_len = max(attended)
+    true_sum = int(sum(lens))
+    results = {}
+    for label, hint in (("split-major", None), ("right sum", true_sum), ("sum 1", 1),
+                        ("larger sum", min(3 * true_sum, B * max_len))):
+        case("compact list %s B%d q%d Hq%d/Hkv%d d%d S=%d causal=%s new=%d, %s" % (
+            dt, B, qlen, hq, hkv, d, S, causal, new_len, label))
+        out, lse = api.decode_fwd(q, kc, vc, bt, sl, num_splits=S, softmax_scale=wl.scale,
+                                  max_seqlen_k=max_len, k_new=kn, v_new=vn, causal=causal,
+                                  sum_seqlen_k=hint)
+        torch.cuda.synchronize()
+        plan = api.last_plan()
+        assert plan.num_splits == S
+        if hint is None:
+            assert plan.extra_blocks == 0 and plan.grid == plan.units * S
+        elif plan.extra_blocks > 0:
+            assert plan.grid == plan.units + plan.extra_blocks < plan.units * S
+        if label in ("right sum", "sum 1"):
+            assert plan.extra_blocks > 0
+        if label == "sum 1":
+            assert plan.extra_blocks == 1
+        o, l = bits_of(out), lse.cpu().numpy()
+        e1 = check_out(o, ref_o, dt, label)
+        e2 = check_lse(l, ref_l)
+        print("  extra_blocks=%d grid=%d max|dO|=%.3g max|dLSE|=%.3g" % (
+            plan.extra_blocks, plan.grid, e1, e2), flush=True)
+        results[label] = (o, l)
+    o0, l0 = results["split-major"]
+    for label, (o, l) in results.items():
+        assert np.array_equal(o, o0) and np.array_equal(l, l0, equal_nan=True), label
+
+
 # ------------------------------------------------------------- varlen Q ----
 
 VARLEN = [
