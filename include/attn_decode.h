@@ -93,7 +93,7 @@ typedef struct {
                             * splits a ragged batch (max_seqlen_k over twice
                             * the mean length) whose longest sequence exceeds
                             * two compute units' fair shares of all keys,
-                            * into pieces of at most half a share (an
+                            * into pieces of at most two thirds of a share (an
                             * addition to the pages' rule), and a split call
                             * may launch the compact list (see
                             * attn_plan.extra_blocks) instead of every

@@ -80,20 +80,24 @@ int rows_per_block(int64_t rows, int head_dim) {
 // sequence (head units x row blocks).  In a ragged batch (longest sequence
 // over twice the mean) whose longest sequence also exceeds two shares, that
 // sequence would outlast the rest of the batch on one workgroup, so it is
-// cut into pieces of at most half a share; shorter sequences keep fewer
-// splits (a split past a sequence's end does nothing).  Uniform batches are
-// left to the pages' rule, which already sizes splits by the common length.
-// Returns the split count this asks for (1 when it does not apply), at most
-// kMaxSplitsRule.  Measured on MI355X (paged, 8 KV heads): 128 sequences of
-// log-uniform length 1..8192 at d 64, 81.7 us at S = 1 and 62.9 at S = 5
-// (this rule's pick); 32 such sequences at d 128, 79.0 and 46.0 (S = 11).
+// cut into pieces of at most two thirds of a share; shorter sequences keep
+// fewer splits (with the length sum the call launches only the splits that
+// hold keys, see the compact list).  Uniform batches are left to the pages'
+// rule, which already sizes splits by the common length.  Returns the split
+// count this asks for (1 when it does not apply), at most kMaxSplitsRule.
+// Measured on MI355X with the compact list (paged, 8 KV heads, lengths
+// log-uniform in 1..8192 or 1..4096), us at half-share pieces -> two-thirds
+// pieces: 128 sequences d 64 54.1 (S 5) -> 53.6 (S 4); 32 sequences d 128
+// 43.0 (S 11) -> 38.1 (S 8); 64 sequences up to 4096 31.4 (S 9) -> 30.0
+// (S 7); 128 sequences d 128 91.5 (S 5) -> 90.1 (S 4); 16 sequences 16.0
+// (S 29) -> 16.1 (S 22).  Unsplit, the first of these takes 76.7 us.
 int ragged_splits(int64_t batch, int64_t streams, int64_t sum_seqlen_k, int64_t max_seqlen_k,
                   int num_cus) {
   if (sum_seqlen_k <= 0 || streams <= 0 || batch <= 0) return 1;
   const double mean = double(sum_seqlen_k) / double(batch);
   const double share = double(streams) * double(sum_seqlen_k) / double(num_cus);
   if (double(max_seqlen_k) <= 2.0 * mean || double(max_seqlen_k) <= 2.0 * share) return 1;
-  const double s = std::ceil(double(max_seqlen_k) / (0.5 * share));
+  const double s = std::ceil(1.5 * double(max_seqlen_k) / share);
   return s >= kMaxSplitsRule ? kMaxSplitsRule : int(s);
 }
 

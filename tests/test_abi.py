@@ -262,11 +262,13 @@ def test_check_paged_inputs(lib):
 RAGGED_CASES = [
     # (name, kwargs, expected S)
     # 128 seqs, 16 q heads / 8 KV heads, d 64: share = 8 * 112861 / 256 =
-    # 3526.9; 7769 > 7053.8; ceil(7769 / 1763.45) = 5; page rule alone: 1
+    # 3526.9; 7769 > 7053.8; ceil(1.5 * 7769 / 3526.9) = ceil(3.30) = 4;
+    # page rule alone: 1
     ("ragged d64", dict(batch=128, q_len=1, hq=16, hkv=8, d=64, maxp=512, max_L=7769,
-                        sum_L=112861), 5),
-    # 32 seqs GQA-4 d 128: share = 8 * 40957 / 256 = 1279.9; ceil(6642 / 639.95) = 11
-    ("ragged d128", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=416, max_L=6642, sum_L=40957), 11),
+                        sum_L=112861), 4),
+    # 32 seqs GQA-4 d 128: share = 8 * 40957 / 256 = 1279.9;
+    # ceil(1.5 * 6642 / 1279.9) = ceil(7.78) = 8
+    ("ragged d128", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=416, max_L=6642, sum_L=40957), 8),
     # near-uniform lengths: share = 8 * 32002 / 256 = 1000.06; 1100 <= 2000: rule's 1
     ("uniform ~1000", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=69, max_L=1100, sum_L=32002), 1),
     # long uniform context, GQA-8: max_L = mean, not ragged: the rule's 14
@@ -275,12 +277,13 @@ RAGGED_CASES = [
     # 8 * 64000 / 256 = 2000, 2400 <= 4000: the rule's 1
     ("ragged under two shares", dict(batch=64, q_len=1, hq=32, hkv=8, maxp=150, max_L=2400,
                                      sum_L=64000), 1),
-    # one long sequence among 255 one-key ones: 510 pieces asked, capped at 128
+    # one long sequence among 255 one-key ones: share = 65791 / 256 = 257.0,
+    # ceil(1.5 * 65536 / 257.0) = 383 pieces asked, capped at 128
     ("cap", dict(batch=256, q_len=1, hq=1, hkv=1, maxp=4096, max_L=65536, sum_L=65536 + 255), 128),
     # 32 query rows per unit (q_len 8, G 4): two row blocks of 16 would be one
     # 32-row block, streams = 8: share = 8 * 40957 / 256, as in "ragged d128"
     ("ragged 32 rows", dict(batch=32, q_len=8, hq=32, hkv=8, maxp=416, max_L=6642,
-                            sum_L=40957), 11),
+                            sum_L=40957), 8),
 ]
 
 
@@ -300,16 +303,16 @@ def test_ragged_hint_plan(lib, name, kw, want):
 
 # Compact list: extra_blocks = max(1, floor(sum / C) * head units * row
 # blocks), used when units + extra_blocks < units * S.  Worked by hand:
-#   ragged d64:  C = 16 * ceil(486 / 5) = 1568; floor(112861 / 1568) = 71;
-#                71 * 8 = 568; 1024 + 568 = 1592 < 5120
-#   ragged d128: C = 16 * ceil(416 / 11) = 608; floor(40957 / 608) = 67;
-#                67 * 8 = 536; 256 + 536 = 792 < 2816
+#   ragged d64:  C = 16 * ceil(486 / 4) = 1952; floor(112861 / 1952) = 57;
+#                57 * 8 = 456; 1024 + 456 = 1480 < 4096
+#   ragged d128: C = 16 * ceil(416 / 8) = 832; floor(40957 / 832) = 49;
+#                49 * 8 = 392; 256 + 392 = 648 < 2048
 #   long uniform: C = 1184; floor(65536 / 1184) * 4 = 220; 16 + 220 = 236 is
 #                not below 16 * 14 = 224: split-major
 #   cap:         C = 512; floor(65791 / 512) = 128; 256 + 128 < 32768
 #   ragged 32 rows: as ragged d128 (one 32-row block per unit)
-COMPACT_EXTRA = {"ragged d64": 568, "ragged d128": 536, "uniform ~1000": 0, "long uniform": 0,
-                 "ragged under two shares": 0, "cap": 128, "ragged 32 rows": 536}
+COMPACT_EXTRA = {"ragged d64": 456, "ragged d128": 392, "uniform ~1000": 0, "long uniform": 0,
+                 "ragged under two shares": 0, "cap": 128, "ragged 32 rows": 392}
 
 
 @pytest.mark.parametrize("name,kw,want", RAGGED_CASES, ids=[c[0] for c in RAGGED_CASES])
