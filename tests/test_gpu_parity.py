@@ -454,10 +454,13 @@ VARLEN = [
 
 @pytest.mark.parametrize("shape", VARLEN, ids=lambda v: "%s-G%d-d%d" % (v[0], v[1] // v[2], v[3]))
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("S", [0, 1, 3])
-def test_varlen_queries(shape, causal, S):
+@pytest.mark.parametrize("S,length_sum", [(0, False), (1, False), (3, False), (0, True),
+                                          (3, True)])
+def test_varlen_queries(shape, causal, S, length_sum):
     """A query count per sequence (cu_seqlens_q), packed; each sequence's
-    expected rows come from the oracle run on that sequence alone."""
+    expected rows come from the oracle run on that sequence alone.  With the
+    length sum the planner splits the longest sequence and the call runs the
+    compact split list."""
     dt, hq, hkv, d, qlens = shape
     lens = [30, 300, 64, 9, 1000]
     B, maxq = len(lens), max(qlens)
@@ -475,12 +478,17 @@ def test_varlen_queries(shape, causal, S):
                                       scale=wl.scale, causal=causal)
         ref_o[cu[b]:cu[b + 1]] = o[0]
         ref_l[:, cu[b]:cu[b + 1]] = l[0]
-    case("varlen q_lens %s, causal=%s S=%d" % (qlens, causal, S))
+    case("varlen q_lens %s, causal=%s S=%d length_sum=%s" % (qlens, causal, S, length_sum))
     out, lse = api.decode_varlen_fwd(to_dev(q, dt), to_dev(wl.k_cache, dt), to_dev(wl.v_cache, dt),
                                      i32_dev(wl.block_table), i32_dev(wl.cache_seqlens),
                                      i32_dev(cu), maxq, num_splits=S, softmax_scale=wl.scale,
-                                     max_seqlen_k=wl.max_seqlen_k, causal=causal)
+                                     max_seqlen_k=wl.max_seqlen_k, causal=causal,
+                                     sum_seqlen_k=sum(lens) if length_sum else None)
     torch.cuda.synchronize()
+    if length_sum:
+        plan = api.last_plan()
+        print("  plan S=%d extra_blocks=%d" % (plan.num_splits, plan.extra_blocks), flush=True)
+        assert plan.extra_blocks > 0
     check_out(bits_of(out), ref_o, dt)
     check_lse(lse.cpu().numpy(), ref_l)
     assert api.last_plan().pack_gqa == 1
@@ -623,21 +631,25 @@ def test_bitwise_determinism_and_page_permutation():
         assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
-def test_hip_graph_replays_match_eager():
+@pytest.mark.parametrize("length_sum", [False, True], ids=["split-major", "compact"])
+def test_hip_graph_replays_match_eager(length_sum):
     """A split call (fused combine, arrival counters rearmed by the kernel,
     no memset) captured in a HIP graph and replayed, with eager calls on
-    other inputs in between: every replay equals the eager result."""
+    other inputs in between: every replay equals the eager result.  With
+    the length sum the call launches the compact split list."""
     wl = W.make_paged(1800, "bf16", 4, 2, 16, 4, 128, 16, [700, 33, 1500, 1], spare_pages=2)
     q, kc, vc = to_dev(wl.q, "bf16"), to_dev(wl.k_cache, "bf16"), to_dev(wl.v_cache, "bf16")
     bt, sl = i32_dev(wl.block_table), i32_dev(wl.cache_seqlens)
     q2 = to_dev(W.make_paged(1801, "bf16", 4, 2, 16, 4, 128, 16, [700, 33, 1500, 1]).q, "bf16")
-    case("HIP graph capture of a 4-split decode call, 5 replays")
+    hint = int(wl.cache_seqlens.sum()) if length_sum else None
+    case("HIP graph capture of a 4-split decode call, 5 replays, length sum %s" % hint)
     call = api.PreparedDecode(q, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
-                              max_seqlen_k=wl.max_seqlen_k)
+                              max_seqlen_k=wl.max_seqlen_k, sum_seqlen_k=hint)
     other = api.PreparedDecode(q2, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
-                               max_seqlen_k=wl.max_seqlen_k)
+                               max_seqlen_k=wl.max_seqlen_k, sum_seqlen_k=hint)
     call()
     torch.cuda.synchronize()
+    assert (api.last_plan().extra_blocks > 0) == length_sum
     ref_o, ref_l = bits_of(call.out).copy(), call.lse.cpu().numpy().copy()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -648,8 +660,7 @@ def test_hip_graph_replays_match_eager():
     g = torch.cuda.CUDAGraph()
     graph_call = api.PreparedDecode(q, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
                                     max_seqlen_k=wl.max_seqlen_k, out=call.out, lse=call.lse,
-                                    workspace=call.workspace,
-                                    stream=None)
+                                    workspace=call.workspace, stream=None, sum_seqlen_k=hint)
     with torch.cuda.graph(g):
         graph_call.args[-1] = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         graph_call()
