@@ -265,7 +265,7 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   }
   // Paged calls whose grid needs more than one round run the first split's
   // sequences longest first (ranked inside its workgroups).
-  prm.by_length = paged && prm.batch <= skv::kMaxOrderBatch && plan.grid > plan.num_cus;
+  prm.by_length = paged && prm.batch <= skv::kMaxRankBatch && plan.grid > plan.num_cus;
   prm.extra_blocks = paged ? plan.extra_blocks : 0;
   if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream) != hipSuccess)
     return ATTN_ERR_HIP;

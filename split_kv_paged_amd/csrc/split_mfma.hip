@@ -706,10 +706,10 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 // short sequences are never launched.  The host sizes extra_blocks from the
 // length sum so that each takes one item; with a smaller count (a wrong
 // sum) they loop over the items, which stays correct.
-// In both, when the grid takes more than one round of workgroups, split 0
-// (the one every sequence has) runs its sequences longest first (a
-// longest-processing-time order): each of its workgroups ranks the batch
-// by length, ties by index.
+// In both, when the grid takes more than one round of workgroups and the
+// batch is small (kMaxRankBatch), split 0 (the one every sequence has) runs
+// its sequences longest first (a longest-processing-time order): each of
+// its workgroups ranks the batch by length, ties by index.
 // The row blocks of one (sequence, head unit) sit 8 workgroups apart:
 // workgroups are dealt to the 8 XCDs round-robin, so they land on the same
 // XCD, close in time, and the second one to read a KV tile finds it in

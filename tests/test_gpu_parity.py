@@ -443,6 +443,31 @@ def test_compact_split_list(spec):
         assert np.array_equal(o, o0) and np.array_equal(l, l0, equal_nan=True), label
 
 
+@pytest.mark.parametrize("length_sum", [False, True], ids=["split-major", "compact"])
+def test_large_ragged_batch_unranked(length_sum):
+    """Over 128 sequences the split-0 workgroups keep the batch order (no
+    length ranking); a multi-round grid, with and without the compact list."""
+    B = 300
+    wl = W.make_paged(1700, "fp16", B, 1, 16, 8, 64, 16,
+                      lambda rng: W.c5_lengths(rng, batch=B, max_len=3000), spare_pages=1)
+    ref = oracle_paged(wl)
+    for S in (0, 3):
+        case("ragged B%d fp16 GQA-2 d64 up to 3000 keys, S=%d, length sum %s" % (
+            B, S, length_sum))
+        q, kc, vc = to_dev(wl.q, "fp16"), to_dev(wl.k_cache, "fp16"), to_dev(wl.v_cache, "fp16")
+        out, lse = api.decode_fwd(q, kc, vc, i32_dev(wl.block_table), i32_dev(wl.cache_seqlens),
+                                  num_splits=S, softmax_scale=wl.scale,
+                                  max_seqlen_k=wl.max_seqlen_k,
+                                  sum_seqlen_k=int(wl.cache_seqlens.sum()) if length_sum else None)
+        torch.cuda.synchronize()
+        plan = api.last_plan()
+        assert plan.grid > plan.num_cus
+        e1 = check_out(bits_of(out), ref[0], "fp16")
+        e2 = check_lse(lse.cpu().numpy(), ref[1])
+        print("  plan S=%d extra=%d grid=%d max|dO|=%.3g max|dLSE|=%.3g" % (
+            plan.num_splits, plan.extra_blocks, plan.grid, e1, e2), flush=True)
+
+
 # ------------------------------------------------------------- varlen Q ----
 
 VARLEN = [
