@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef enum {
     ATTN_OK = 0,
@@ -97,7 +97,9 @@ typedef struct {
                             * addition to the pages' rule), and a split call
                             * may launch the compact list (see
                             * attn_plan.extra_blocks) instead of every
-                            * (unit, split) pair.  0 <= sum <= batch *
+                            * (unit, split) pair, and a head-dim-64 call may
+                            * read two KV heads per unit (attn_plan.
+                            * head_pair).  0 <= sum <= batch *
                             * max_seqlen_k, else ATTN_ERR_SHAPE; a wrong but
                             * in-range value changes only speed. */
 } attn_decode_shape;
@@ -124,11 +126,14 @@ typedef struct {
     int32_t num_splits;      /* S: KV ranges per (sequence, head unit)        */
     int32_t pack_gqa;        /* 1: the G query heads of a KV head share a unit */
     int32_t rows_per_unit;   /* query rows per unit: q_len*G packed, q_len not */
+                             /* (head pairs: q_len*2G)                         */
     int32_t rows_per_block;  /* packed rows one workgroup carries: 16; at      */
                              /* head_dim 64 or 128, 32 for units of 17..32     */
                              /* rows and 64 beyond (KV read once per block)    */
     int32_t row_blocks;      /* ceil(rows_per_unit / rows_per_block)           */
-    int32_t units;           /* batch * head units * row_blocks               */
+    int32_t units;           /* batch * head units * row_blocks; a head unit  */
+                             /* is a KV head (packed), a query head, or a pair */
+                             /* of KV heads (head_pair)                        */
     int32_t grid;            /* workgroups of the split kernel: units * S, or */
                              /* units + extra_blocks with the compact list    */
     int32_t split_granule;   /* split lengths are multiples of this many keys  */
@@ -138,10 +143,18 @@ typedef struct {
                              /* finish (1, a separate launch, is not used)     */
     int32_t kernel;          /* diagnostic: 10000 (16-byte loads), 20000      */
                              /* (16-byte loads, head_dim a multiple of 8 below */
-                             /* the tile's) or 30000 (element loads) + 1000 if */
-                             /* paged + tile head dim (32, 64, 128 or 256)     */
+                             /* the tile's), 30000 (element loads) or 40000    */
+                             /* (head pairs) + 1000 if paged + tile head dim  */
+                             /* (32, 64, 128 or 256)                          */
     int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
+    int32_t head_pair;       /* 1: paged, head_dim 64, an even num_heads_kv,  */
+                             /* packed, q_len * 2G <= 16 and sum_seqlen_k     */
+                             /* given: a unit is two                          */
+                             /* adjacent KV heads, read as one 128-wide key   */
+                             /* row (the cache puts them side by side), with  */
+                             /* both heads' 2G * q_len query rows; units,     */
+                             /* rows_per_unit and the split rule count pairs  */
     int32_t extra_blocks;    /* 0: the grid is split-major, every (unit,      */
                              /* split) pair has a workgroup (empty splits     */
                              /* return at once).  > 0 (paged, S > 1, length   */

@@ -193,7 +193,20 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   constexpr bool kDma = NBUF == 0;
   static_assert(!kDma || (kSwz && GEN != 2), "direct-to-LDS tiles need >= 8 16-byte chunks a row");
   static_assert(D % 32 == 0, "head_dim");
-  const int hd = GEN ? p.head_dim : D;  // elements per key / query / output row
+  // GEN 3 (paged, head pairs): two adjacent KV heads of head dim D / 2 are
+  // one D-wide key row (the cache layout puts them side by side), and the
+  // unit packs both heads' query rows.  A row's D / 2 query values sit in
+  // its own head's half of the D columns and the other half is zero, so its
+  // scores see only its head's keys; its output is the same half of O.
+  constexpr bool kPair = GEN == 3;
+  static_assert(!kPair || (PAGED && NRB == 1), "head pairs: paged, one row block");
+  const int hd = GEN == 0 ? D : kPair ? D / 2 : p.head_dim;  // query / output row
+  const int kvd = GEN == 1 || GEN == 2 ? p.head_dim : D;     // key / value row
+  // first tile column of packed row pr's head (head pairs: the second half
+  // for the second head's G = heads_per_unit / 2 rows)
+  auto col0 = [&](int pr) {
+    return kPair ? ((pr % p.heads_per_unit) >= (p.heads_per_unit >> 1) ? D / 2 : 0) : 0;
+  };
 
   struct Buf {
     uint4 k[KB];
@@ -311,10 +324,12 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       }
     } else {
       const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd);
+      const int c0 = col0(rowq) / 8;  // first 16-byte chunk of this row's half (head pairs)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        qb[r][kb] = (real && (GEN == 0 || chunk(g, kb) * 8 < hd)) ? qp[chunk(g, kb)]
-                                                                 : make_uint4(0, 0, 0, 0);
+      for (int kb = 0; kb < KB; ++kb) {
+        const int c = chunk(g, kb) - c0;
+        qb[r][kb] = (real && c >= 0 && (GEN == 0 || c * 8 < hd)) ? qp[c] : make_uint4(0, 0, 0, 0);
+      }
     }
   }
 
@@ -329,7 +344,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
     l32[r] = 0.f;
   }
 
-  const long row_stride = PAGED ? (long)p.hkv * hd : (long)hd;
+  const long row_stride = PAGED ? (long)p.hkv * kvd : (long)kvd;
   const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.k);
   const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(p.v);
   const int voff = int(n16 * row_stride * 2);  // key n16 of the tile
@@ -358,9 +373,9 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   auto tile_row0 = [&](int idx, int page) -> long {
     const int tt = t0 + (wave + idx * NW) * kTile;
     if constexpr (PAGED) {
-      return ((long)page * p.page_size + tt % p.page_size) * p.hkv * hd + (long)h * hd;
+      return ((long)page * p.page_size + tt % p.page_size) * p.hkv * kvd + (long)h * kvd;
     } else {
-      return ((long)h * p.kv_len + tt) * hd;
+      return ((long)h * p.kv_len + tt) * kvd;
     }
   };
 
@@ -380,8 +395,8 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c0 = chunk(g, kb) * 8 + 2 * e;
-          const int o0 = c0 < hd ? int((n16 * row_stride + c0) * 2) : kPastEnd;
-          const int o1 = c0 + 1 < hd ? int((n16 * row_stride + c0 + 1) * 2) : kPastEnd;
+          const int o0 = c0 < kvd ? int((n16 * row_stride + c0) * 2) : kPastEnd;
+          const int o1 = c0 + 1 < kvd ? int((n16 * row_stride + c0 + 1) * 2) : kPastEnd;
           wk[e] = load2(rk, o0) | (load2(rk, o1) << 16);
           wv[e] = load2(rv, o0) | (load2(rv, o1) << 16);
         }
@@ -392,7 +407,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int ck = chunk(g, kb);
-        const int off = (GEN == 0 || ck * 8 < hd) ? voff + ck * 16 : kPastEnd;
+        const int off = (GEN == 0 || ck * 8 < kvd) ? voff + ck * 16 : kPastEnd;
         bf.k[kb] = load16(rk, off);
         bf.v[kb] = load16(rv, off);
       }
@@ -505,7 +520,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
     for (int j = 0; j < KB; ++j) {
       const int row = j * kRPI + lane / kCPR;
       const int ch = (lane % kCPR) ^ (2 * (row & 3) + ((row >> 2) & 1));
-      const int off = (GEN == 0 || ch * 8 < hd) ? int(row * row_stride * 2) + ch * 16 : kPastEnd;
+      const int off = (GEN == 0 || ch * 8 < kvd) ? int(row * row_stride * 2) + ch * 16 : kPastEnd;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(my_k + j * 1024), 16, off, 0, 0, kStream);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(my_v + j * 1024), 16, off, 0, 0, kStream);
     }
@@ -601,6 +616,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       const int r = t / hd;
       const int d = t % hd;
       const int pr = row0 + 16 * blk + r;
+      const int col = col0(pr) + d;
       float Mx = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][r]);
@@ -609,7 +625,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const float f = (s_m[w][r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - Mx);
-          num = fmaf(f, s_acc[((long)w * RMAX + r) * D + d], num);
+          num = fmaf(f, s_acc[((long)w * RMAX + r) * D + col], num);
           den = fmaf(f, s_l32[w][r], den);
         }
       }
@@ -855,6 +871,12 @@ hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
 template <int DT, bool PAGED>
 hipError_t launch_mfma_dt(const SplitParams& p, int grid, hipStream_t s) {
   const int d = p.head_dim;
+  if (p.head_pair) {  // two head-dim-64 KV heads per 128-wide tile
+    if constexpr (PAGED) {
+      if (d == 64 && p.nrb == 1) return launch_mfma_k<DT, 128, PAGED, 3, 1>(p, grid, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (d) {
     case 32: return launch_mfma_d<DT, 32, PAGED, 0>(p, grid, s);
     case 64: return launch_mfma_d<DT, 64, PAGED, 0>(p, grid, s);

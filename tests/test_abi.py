@@ -131,11 +131,54 @@ def test_plan_fields_are_consistent(lib):
     assert plan.rows_per_unit == 2 and plan.units == 2 * 8
 
 
+@pytest.mark.parametrize("kw,pair", [
+    (dict(q_len=1, hq=8, hkv=2), 1),     # G 4: 8 rows per pair
+    (dict(q_len=2, hq=8, hkv=2), 1),     # 16 rows per pair: still one block
+    (dict(q_len=3, hq=8, hkv=2), 0),     # 24 rows: no pair
+    (dict(q_len=1, hq=16, hkv=2), 1),    # G 8: 16 rows
+    (dict(q_len=1, hq=32, hkv=2), 0),    # G 16: 32 rows
+    (dict(q_len=1, hq=6, hkv=3), 0),     # an odd number of KV heads
+    (dict(q_len=1, hq=8, hkv=8), 0),     # MHA decode is not packed (rule): no pair
+    (dict(q_len=1, hq=8, hkv=2, pack=0), 0),
+    (dict(q_len=1, hq=8, hkv=2, d=128), 0),
+    (dict(q_len=1, hq=8, hkv=2, d=96), 0),
+])
+def test_head_pair_plan(lib, kw, pair):
+    """Paged head dim 64 with the length sum: two adjacent KV heads per unit
+    when the pair's packed rows fit one 16-row block; units, rows and the
+    split rule then count pairs.  Without the sum, no pairs."""
+    kw = dict(kw)
+    d = kw.pop("d", 64)
+    code, plan = _plan(lib, batch=3, max_L=512, maxp=32, d=d, **kw)
+    assert code == 0 and plan.head_pair == 0
+    code, plan = _plan(lib, batch=3, max_L=512, maxp=32, d=d, sum_L=1200, **kw)
+    assert code == 0 and plan.head_pair == pair
+    G = kw["hq"] // kw["hkv"]
+    if pair:
+        assert plan.pack_gqa == 1 and plan.rows_per_unit == kw["q_len"] * 2 * G
+        assert plan.units == 3 * (kw["hkv"] // 2) and plan.kernel == 41128
+        assert plan.rows_per_block == 16 and plan.row_blocks == 1
+        # the split rule sees the pairs: the pages' rule with Hkv / 2 and 2G
+        want = oplan.plan(3, kw["q_len"], kw["hq"], kw["hkv"] // 2, 512, 256, 16, 128)
+        assert (plan.num_splits, bool(plan.pack_gqa)) == want
+    # the workspace holds head_dim-wide partials of the real query rows
+    code, plan = _plan(lib, batch=3, max_L=4096, maxp=256, d=d, S=3, sum_L=9000, **kw)
+    nrows = 3 * kw["q_len"] * kw["hq"]
+    o = (3 * nrows * d * 4 + 255) // 256 * 256
+    assert plan.workspace_bytes == o + (3 * nrows * 4 + 255) // 256 * 256 + (
+        (plan.units * 4 + 255) // 256 * 256)
+
+
 def test_plan_kernel_ids_name_the_tile_and_load_path(lib):
     for d, want in [(64, 11064), (128, 11128), (32, 11032), (256, 11256), (96, 21128),
                     (1, 31032), (200, 21256), (33, 31064), (16, 21032), (130, 31256)]:
         code, plan = _plan(lib, batch=2, q_len=1, hq=8, hkv=2, max_L=512, maxp=32, d=d)
         assert code == 0 and plan.kernel == want, (d, plan.kernel)
+    # with the length sum, d 64 with two KV heads: a head pair on the 128-wide tile
+    code, plan = _plan(lib, batch=2, q_len=1, hq=8, hkv=2, max_L=512, maxp=32, d=64, sum_L=900)
+    assert code == 0 and plan.kernel == 41128 and plan.head_pair == 1
+    code, plan = _plan(lib, batch=2, q_len=1, hq=4, hkv=1, max_L=512, maxp=32, d=64, sum_L=900)
+    assert code == 0 and plan.kernel == 11064 and plan.head_pair == 0  # one KV head
     shape = L.DenseShape(8, 2, 1, 512, 80, 0)
     plan = L.Plan()
     assert lib.attn_dense_plan(ctypes.byref(shape), 0, 0, ctypes.byref(plan)) == 0
@@ -261,11 +304,11 @@ def test_check_paged_inputs(lib):
 # shapes below.
 RAGGED_CASES = [
     # (name, kwargs, expected S)
-    # 128 seqs, 16 q heads / 8 KV heads, d 64: share = 8 * 112861 / 256 =
-    # 3526.9; 7769 > 7053.8; ceil(1.5 * 7769 / 3526.9) = ceil(3.30) = 4;
-    # page rule alone: 1
+    # 128 seqs, 16 q heads / 8 KV heads, d 64 as 4 head pairs: share =
+    # 4 * 112861 / 256 = 1763.45; 7769 > 3526.9; ceil(1.5 * 7769 / 1763.45) =
+    # ceil(6.61) = 7; page rule alone: 1
     ("ragged d64", dict(batch=128, q_len=1, hq=16, hkv=8, d=64, maxp=512, max_L=7769,
-                        sum_L=112861), 4),
+                        sum_L=112861), 7),
     # 32 seqs GQA-4 d 128: share = 8 * 40957 / 256 = 1279.9;
     # ceil(1.5 * 6642 / 1279.9) = ceil(7.78) = 8
     ("ragged d128", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=416, max_L=6642, sum_L=40957), 8),
@@ -295,23 +338,24 @@ def test_ragged_hint_plan(lib, name, kw, want):
     # without the hint the pages' rule alone decides
     kw0 = dict(kw, sum_L=0)
     code0, plan0 = _plan(lib, **kw0)
-    ref_splits, _ = oplan.plan(kw["batch"], kw["q_len"], kw["hq"], kw["hkv"], kw["max_L"], 256,
-                               16, 128)
+    hkv = kw["hkv"] // 2 if plan0.head_pair else kw["hkv"]  # the rule counts head pairs
+    ref_splits, _ = oplan.plan(kw["batch"], kw["q_len"], kw["hq"], hkv, kw["max_L"], 256, 16,
+                               128)
     assert plan0.num_splits == ref_splits
     assert plan.num_splits >= plan0.num_splits
 
 
 # Compact list: extra_blocks = max(1, floor(sum / C) * head units * row
 # blocks), used when units + extra_blocks < units * S.  Worked by hand:
-#   ragged d64:  C = 16 * ceil(486 / 4) = 1952; floor(112861 / 1952) = 57;
-#                57 * 8 = 456; 1024 + 456 = 1480 < 4096
+#   ragged d64:  4 head pairs; C = 16 * ceil(486 / 7) = 1120;
+#                floor(112861 / 1120) = 100; 100 * 4 = 400; 512 + 400 = 912 < 3584
 #   ragged d128: C = 16 * ceil(416 / 8) = 832; floor(40957 / 832) = 49;
 #                49 * 8 = 392; 256 + 392 = 648 < 2048
 #   long uniform: C = 1184; floor(65536 / 1184) * 4 = 220; 16 + 220 = 236 is
 #                not below 16 * 14 = 224: split-major
 #   cap:         C = 512; floor(65791 / 512) = 128; 256 + 128 < 32768
 #   ragged 32 rows: as ragged d128 (one 32-row block per unit)
-COMPACT_EXTRA = {"ragged d64": 456, "ragged d128": 392, "uniform ~1000": 0, "long uniform": 0,
+COMPACT_EXTRA = {"ragged d64": 400, "ragged d128": 392, "uniform ~1000": 0, "long uniform": 0,
                  "ragged under two shares": 0, "cap": 128, "ragged 32 rows": 392}
 
 
@@ -324,10 +368,13 @@ def test_compact_list_plan(lib, name, kw, want):
         assert plan.grid == plan.units + plan.extra_blocks < plan.units * plan.num_splits
     else:
         assert plan.grid == plan.units * plan.num_splits
-    # the compact list changes the grid only: same splits, same workspace
+    # the compact list changes the grid only: same splits and partials (head
+    # pairs, which also wait for the sum, halve the arrival counters)
     code0, plan0 = _plan(lib, **dict(kw, sum_L=0, S=plan.num_splits))
     assert plan0.extra_blocks == 0 and plan0.grid == plan0.units * plan0.num_splits
-    assert plan0.workspace_bytes == plan.workspace_bytes
+    counters = lambda p: (p.units * 4 + 255) // 256 * 256 if p.num_splits > 1 else 0
+    assert (plan0.workspace_bytes - counters(plan0)) == (plan.workspace_bytes - counters(plan))
+    assert plan0.units == plan.units * (2 if plan.head_pair else 1)
     assert plan0.split_keys == plan.split_keys
     # a batch over 1024 sequences keeps the split-major grid
     if plan.num_splits > 1:

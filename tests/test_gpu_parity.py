@@ -468,6 +468,62 @@ def test_large_ragged_batch_unranked(length_sum):
             plan.num_splits, plan.extra_blocks, plan.grid, e1, e2), flush=True)
 
 
+PAIRS = [
+    # dtype, B, q_len, Hq, Hkv, lengths, causal, new_len
+    ("fp16", 5, 1, 16, 8, [1, 17, 700, 2000, 64], False, 0),    # G 2: 4 rows per pair
+    ("bf16", 4, 1, 32, 4, [300, 1025, 9, 4000], False, 0),      # G 8: 16 rows
+    ("bf16", 3, 2, 16, 4, [500, 33, 1800], True, 0),            # q_len 2, causal: 16 rows
+    ("fp16", 3, 1, 8, 2, [100, 2047, 5], False, 3),             # keys appended first
+]
+
+
+@pytest.mark.parametrize("spec", PAIRS, ids=lambda c: "%s-B%d-q%d-G%d-new%d" % (
+    c[0], c[1], c[2], c[3] // c[4], c[7]))
+@pytest.mark.parametrize("S", [1, 3])
+def test_head_pairs(spec, S):
+    """Head dim 64 with an even number of KV heads and the length sum: a
+    unit is a pair of adjacent KV heads on the 128-wide tile, each query row
+    in its head's half.  The output matches the oracle and, bit for bit, the unpacked
+    call (one query head per unit on the 64-wide tile): the pair only adds
+    exact zeros to each score."""
+    dt, B, qlen, hq, hkv, lens, causal, new_len = spec
+    d = 64
+    if new_len:
+        wl, k_new, v_new, kc_h, vc_h = _append_case(1900 + B, dt, B, qlen, hq, hkv, d, lens,
+                                                    new_len)
+        sl_h = np.array(lens, dtype=np.int32)
+    else:
+        wl = W.make_paged(1900 + B, dt, B, qlen, hq, hkv, d, 16, lens, spare_pages=1,
+                          outlier_p=0.01)
+        kc_h, vc_h, k_new, v_new, sl_h = wl.k_cache, wl.v_cache, None, None, wl.cache_seqlens
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    q = to_dev(wl.q, dt)
+    kc, vc = to_dev(kc_h, dt), to_dev(vc_h, dt)
+    bt, sl = i32_dev(wl.block_table), i32_dev(sl_h)
+    kn = to_dev(k_new, dt) if new_len else None
+    vn = to_dev(v_new, dt) if new_len else None
+    got = {}
+    for pack in (-1, 0):
+        case("head pairs %s B%d q%d Hq%d/Hkv%d S=%d causal=%s new=%d pack=%d" % (
+            dt, B, qlen, hq, hkv, S, causal, new_len, pack))
+        out, lse = api.decode_fwd(q, kc, vc, bt, sl, num_splits=S, pack_gqa=pack,
+                                  softmax_scale=wl.scale, max_seqlen_k=wl.max_seqlen_k,
+                                  k_new=kn, v_new=vn, causal=causal,
+                                  sum_seqlen_k=int(wl.cache_seqlens.sum()))
+        torch.cuda.synchronize()
+        plan = api.last_plan()
+        assert plan.head_pair == (1 if pack == -1 else 0)
+        o, l = bits_of(out), lse.cpu().numpy()
+        e1 = check_out(o, ref_o, dt)
+        e2 = check_lse(l, ref_l)
+        print("  pair=%d units=%d max|dO|=%.3g max|dLSE|=%.3g" % (plan.head_pair, plan.units,
+                                                               e1, e2), flush=True)
+        got[pack] = (o, l)
+    assert np.array_equal(got[-1][0], got[0][0])
+    assert np.array_equal(got[-1][1], got[0][1], equal_nan=True)
+
+
 # ------------------------------------------------------------- varlen Q ----
 
 VARLEN = [
