@@ -1,8 +1,9 @@
 // split_mfma.hip -- split-KV decode / small-query attention on gfx950 matrix cores.
 //
-// Work unit: (sequence, head unit, block of 16 packed query rows, split).  A
-// head unit is one KV head with its G query heads packed into the rows
-// (pack_gqa) or one query head.  One workgroup per unit; its waves take the
+// Work unit: (sequence, head unit, block of 16, 32 or 64 packed query rows,
+// split).  A head unit is one KV head with its G query heads packed into the
+// rows (pack_gqa), one query head, or (head dim 64) a pair of adjacent KV
+// heads read as one 128-wide key row.  One workgroup per unit; its waves take the
 // 16-key tiles of the split's key range round-robin, each with its own online
 // softmax state, and merge through LDS at the end.  The two contractions run
 // on the matrix cores:
@@ -24,7 +25,7 @@
 //       ds_read_b64_tr_b16, which delivers the key-major B operand.
 //
 // Tile loads.  With 16-byte chunks and at least 8 of them a key row (head
-// dims 64..256, GEN 0/1), K and V go from memory straight into the wave's
+// dims 64..256, GEN 0/1/3), K and V go from memory straight into the wave's
 // LDS slot with 16-byte buffer loads to LDS: each instruction fills 1 KB,
 // whole key rows, so every load touches whole cache lines, and no register
 // holds a tile in flight.  A wave reads tile n out of its slot (K in the
@@ -38,8 +39,8 @@
 // table, 64 tiles' worth per vector load, broadcast with readlane.
 //
 // Packed query rows beyond the unit's real rows are zero; their lanes do the
-// same (SIMD) work and are never written.  A workgroup carries one or two
-// 16-row blocks (NRB) of one unit.
+// same (SIMD) work and are never written.  A workgroup carries one, two or
+// four 16-row blocks (NRB) of one unit.
 //
 // Sources: attention definition (SmallQ FlashAttention README, section 接口);
 // online softmax with max offset (ai6s.net FlashAttention article, section
@@ -167,9 +168,13 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
 //   0  head_dim == D: 16-byte loads;
 //   1  head_dim a multiple of 8 (rows stay 16-byte aligned): 16-byte loads,
 //      a chunk past the head dim gets an offset past the buffer range;
-//   2  any other head_dim: 16-bit element loads.
+//   2  any other head_dim: 16-bit element loads;
+//   3  head pairs (paged, D = 128, head_dim 64): 16-byte loads of whole
+//      128-wide rows of two adjacent KV heads.
 // NRB: 16-row blocks a workgroup carries (1; 2 or 4 when a unit has more
 // than 16 or 32 packed rows, so its KV is read once for up to 64 rows).
+// tid: the thread index (passed in so that the compact list's loop can
+// hide it from loop-invariant hoisting).
 template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB>
 __device__ __forceinline__ void split_unit(const SplitParams& p, const int split, const int b,
                                            const int uh, const int rb, const int tid) {
