@@ -14,14 +14,16 @@ bytes to what the same counter reads for a plain device-to-device copy of
 known size in the same run (on gfx950 FETCH_SIZE counts a 128-byte read
 request as 64 bytes, so the raw figure is about half the real traffic).  The
 summary ends with ``key: value`` lines that bench.py reads back, including a
-digest of the kernel sources: once the sources change, the figure no longer
-describes the built kernel and bench.py reports no traffic.
+digest of the kernel sources' code (comments and layout ignored): once the
+code changes, the figure no longer describes the built kernel and bench.py
+reports no traffic.
 """
 import argparse
 import collections
 import glob
 import hashlib
 import os
+import re
 import sqlite3
 import sys
 
@@ -29,14 +31,30 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
 
+_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|(?://[^\n]*|/\*.*?\*/|\s)+', re.S)
+
+
+def code_text(text):
+    """C++ source with comments removed and whitespace runs collapsed to
+    one space (string literals kept as written), so that a digest of it
+    changes with the code and not with its comments or layout."""
+    def keep(m):
+        t = m.group(0)
+        if t.startswith('"'):
+            return t
+        return " "
+    return _TOKENS.sub(keep, text).strip()
+
+
 def source_digest():
-    """sha256 over the kernel and host sources of the library (csrc/)."""
+    """sha256 over the code (comments and layout ignored) of the library's
+    kernel and host sources (csrc/)."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
         if path.endswith((".hip", ".cpp", ".h")):
             h.update(os.path.basename(path).encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,6 +11,27 @@ sys.path.insert(0, ROOT)
 from split_kv_paged_amd import profiling  # noqa: E402
 
 
+def test_code_text_drops_comments_and_layout_only():
+    a = "int f(int x) {  // one\n  return x + 1; /* two\n lines */ }\n"
+    b = "int f(int x) { return x + 1; }"
+    assert profiling.code_text(a) == profiling.code_text(b) == "int f(int x) { return x + 1; }"
+    # code changes still show, and string literals keep their text
+    assert profiling.code_text("return x + 2;") != profiling.code_text("return x + 1;")
+    s = 'const char* u = "a // b /* c */";'
+    assert profiling.code_text(s) == s
+
+
+def test_source_digest_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("// header\n__global__ void k() {}\n")
+    monkeypatch.setattr(profiling, "CSRC", str(tmp_path))
+    d0 = profiling.source_digest()
+    src.write_text("// another header\n\n__global__   void k() {}  /* note */\n")
+    assert profiling.source_digest() == d0
+    src.write_text("__global__ void k() { int x = 0; }\n")
+    assert profiling.source_digest() != d0
+
+
 def test_source_digest_is_stable_and_short():
     a = profiling.source_digest()
     assert a == profiling.source_digest() and len(a) == 16
