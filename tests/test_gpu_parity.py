@@ -530,6 +530,7 @@ VARLEN = [
     # dtype, Hq, Hkv, d, q lens
     ("bf16", 16, 4, 128, [1, 4, 0, 7, 2]),   # G 4: up to 28 rows (a 32-row block)
     ("fp16", 32, 4, 64, [6, 1, 5, 0, 8]),    # G 8: up to 64 rows (a 64-row block)
+    ("fp16", 8, 4, 64, [1, 4, 0, 3, 2]),     # G 2: with the length sum, head pairs (16 rows)
 ]
 
 
@@ -568,8 +569,10 @@ def test_varlen_queries(shape, causal, S, length_sum):
     torch.cuda.synchronize()
     if length_sum:
         plan = api.last_plan()
-        print("  plan S=%d extra_blocks=%d" % (plan.num_splits, plan.extra_blocks), flush=True)
+        print("  plan S=%d extra_blocks=%d head_pair=%d" % (
+            plan.num_splits, plan.extra_blocks, plan.head_pair), flush=True)
         assert plan.extra_blocks > 0
+        assert plan.head_pair == (1 if (d == 64 and hq // hkv * maxq * 2 <= 16) else 0)
     check_out(bits_of(out), ref_o, dt)
     check_lse(lse.cpu().numpy(), ref_l)
     assert api.last_plan().pack_gqa == 1
