@@ -380,6 +380,7 @@ COMPACT = [
     # dtype, B, q_len, Hq, Hkv, d, lengths, S, causal, new_len
     ("fp16", 12, 1, 16, 8, 64, [8000, 1, 5, 3000, 0, 17, 1500, 2, 6000, 40, 999, 4000], 5,
      False, 0),
+    ("bf16", 9, 1, 32, 8, 128, [5000, 2, 900, 4100, 31, 64, 2500, 7, 3333], 6, False, 0),
     ("bf16", 6, 8, 32, 8, 128, [3000, 10, 2500, 1, 700, 4000], 4, True, 0),  # 32-row blocks
     ("fp16", 5, 8, 64, 8, 64, [2000, 5, 1800, 33, 900], 3, True, 0),         # 64-row blocks
     ("bf16", 4, 4, 32, 8, 128, [1000, 13, 500, 1020], 4, True, 4),           # appended keys
@@ -469,16 +470,17 @@ def test_large_ragged_batch_unranked(length_sum):
 
 
 PAIRS = [
-    # dtype, B, q_len, Hq, Hkv, lengths, causal, new_len
-    ("fp16", 5, 1, 16, 8, [1, 17, 700, 2000, 64], False, 0),    # G 2: 4 rows per pair
-    ("bf16", 4, 1, 32, 4, [300, 1025, 9, 4000], False, 0),      # G 8: 16 rows
-    ("bf16", 3, 2, 16, 4, [500, 33, 1800], True, 0),            # q_len 2, causal: 16 rows
-    ("fp16", 3, 1, 8, 2, [100, 2047, 5], False, 3),             # keys appended first
+    # dtype, B, q_len, Hq, Hkv, lengths, causal, new_len, page size
+    ("fp16", 5, 1, 16, 8, [1, 17, 700, 2000, 64], False, 0, 16),    # G 2: 4 rows per pair
+    ("bf16", 4, 1, 32, 4, [300, 1025, 9, 4000], False, 0, 16),      # G 8: 16 rows
+    ("bf16", 3, 2, 16, 4, [500, 33, 1800], True, 0, 16),            # q_len 2, causal: 16 rows
+    ("fp16", 3, 1, 8, 2, [100, 2047, 5], False, 3, 16),             # keys appended first
+    ("bf16", 4, 1, 16, 4, [100, 1500, 47, 999], False, 0, 48),      # 48-key pages
 ]
 
 
-@pytest.mark.parametrize("spec", PAIRS, ids=lambda c: "%s-B%d-q%d-G%d-new%d" % (
-    c[0], c[1], c[2], c[3] // c[4], c[7]))
+@pytest.mark.parametrize("spec", PAIRS, ids=lambda c: "%s-B%d-q%d-G%d-new%d-P%d" % (
+    c[0], c[1], c[2], c[3] // c[4], c[7], c[8]))
 @pytest.mark.parametrize("S", [1, 3])
 def test_head_pairs(spec, S):
     """Head dim 64 with an even number of KV heads and the length sum: a
@@ -486,14 +488,15 @@ def test_head_pairs(spec, S):
     in its head's half.  The output matches the oracle and, bit for bit, the unpacked
     call (one query head per unit on the 64-wide tile): the pair only adds
     exact zeros to each score."""
-    dt, B, qlen, hq, hkv, lens, causal, new_len = spec
+    dt, B, qlen, hq, hkv, lens, causal, new_len, page = spec
     d = 64
     if new_len:
+        assert page == 16
         wl, k_new, v_new, kc_h, vc_h = _append_case(1900 + B, dt, B, qlen, hq, hkv, d, lens,
                                                     new_len)
         sl_h = np.array(lens, dtype=np.int32)
     else:
-        wl = W.make_paged(1900 + B, dt, B, qlen, hq, hkv, d, 16, lens, spare_pages=1,
+        wl = W.make_paged(1900 + B, dt, B, qlen, hq, hkv, d, page, lens, spare_pages=1,
                           outlier_p=0.01)
         kc_h, vc_h, k_new, v_new, sl_h = wl.k_cache, wl.v_cache, None, None, wl.cache_seqlens
     ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
