@@ -97,9 +97,9 @@ typedef struct {
                             * addition to the pages' rule), and a split call
                             * may launch the compact list (see
                             * attn_plan.extra_blocks) instead of every
-                            * (unit, split) pair, and a head-dim-64 call may
-                            * read two KV heads per unit (attn_plan.
-                            * head_pair).  0 <= sum <= batch *
+                            * (unit, split) pair, and a head-dim-64 or -32
+                            * call may read 2 or 4 KV heads per unit
+                            * (attn_plan.heads_per_row).  0 <= sum <= batch *
                             * max_seqlen_k, else ATTN_ERR_SHAPE; a wrong but
                             * in-range value changes only speed. */
 } attn_decode_shape;
@@ -132,8 +132,8 @@ typedef struct {
                              /* rows and 64 beyond (KV read once per block)    */
     int32_t row_blocks;      /* ceil(rows_per_unit / rows_per_block)           */
     int32_t units;           /* batch * head units * row_blocks; a head unit  */
-                             /* is a KV head (packed), a query head, or a pair */
-                             /* of KV heads (head_pair)                        */
+                             /* is a KV head (packed), a query head, or a     */
+                             /* group of KV heads (heads_per_row > 1)          */
     int32_t grid;            /* workgroups of the split kernel: units * S, or */
                              /* units + extra_blocks with the compact list    */
     int32_t split_granule;   /* split lengths are multiples of this many keys  */
@@ -144,17 +144,19 @@ typedef struct {
     int32_t kernel;          /* diagnostic: 10000 (16-byte loads), 20000      */
                              /* (16-byte loads, head_dim a multiple of 8 below */
                              /* the tile's), 30000 (element loads) or 40000    */
-                             /* (head pairs) + 1000 if paged + tile head dim  */
+                             /* (head groups) + 1000 if paged + tile head dim */
                              /* (32, 64, 128 or 256)                          */
     int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
-    int32_t head_pair;       /* 1: paged, head_dim 64, an even num_heads_kv,  */
-                             /* packed, q_len * 2G <= 16 and sum_seqlen_k     */
-                             /* given: a unit is two                          */
-                             /* adjacent KV heads, read as one 128-wide key   */
-                             /* row (the cache puts them side by side), with  */
-                             /* both heads' 2G * q_len query rows; units,     */
-                             /* rows_per_unit and the split rule count pairs  */
+    int32_t heads_per_row;   /* KV heads per unit: 1, or R = 2 (head_dim 64) */
+                             /* or 4 (head_dim 32) when the call is paged,    */
+                             /* num_heads_kv is a multiple of R, packed,      */
+                             /* q_len * R * G <= 16 and sum_seqlen_k is       */
+                             /* given: the R adjacent KV heads are read as    */
+                             /* one 128-wide key row (the cache puts them     */
+                             /* side by side), with all R heads' query rows;  */
+                             /* units, rows_per_unit and the split rule then  */
+                             /* count these head groups                       */
     int32_t extra_blocks;    /* 0: the grid is split-major, every (unit,      */
                              /* split) pair has a workgroup (empty splits     */
                              /* return at once).  > 0 (paged, S > 1, length   */

@@ -103,10 +103,10 @@ int ragged_splits(int64_t batch, int64_t streams, int64_t sum_seqlen_k, int64_t 
 
 // Diagnostic kernel id: 10000 (16-byte loads), 20000 (16-byte loads with a
 // column mask: head_dim a multiple of 8), 30000 (element loads: any other
-// head_dim) or 40000 (head pairs) + 1000 if paged + the tile head dim
+// head_dim) or 40000 (head groups) + 1000 if paged + the tile head dim
 // (32/64/128/256).
-int kernel_id(int head_dim, bool paged, bool pair) {
-  if (pair) return 40000 + 1000 + 128;
+int kernel_id(int head_dim, bool paged, bool grouped) {
+  if (grouped) return 40000 + 1000 + 128;
   const bool exact = head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
   const int loads = exact ? 10000 : head_dim % 8 == 0 ? 20000 : 30000;
   const int tile = head_dim <= 32 ? 32 : head_dim <= 64 ? 64 : head_dim <= 128 ? 128 : 256;
@@ -129,22 +129,28 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
     pack = should_pack_gqa(varlen, q_len, group, kBlockM);
   else
     pack = pack_gqa == 1;
-  // Head pairs (paged, head_dim 64, an even number of KV heads, packed,
-  // both heads' rows within one 16-row block, and the length sum given):
-  // two adjacent KV heads are one 128-wide key row in the cache, so a
-  // workgroup reads 256 contiguous bytes per key instead of 128, and half
-  // as many workgroups move the same bytes.  Measured on MI355X (paged
-  // fp16): GQA-4, 64 sequences of 2048 keys, 53.7 -> 46.8 us; the ragged
-  // 128-sequence GQA-2 batch with its length sum, 54.0 -> 48.7 us.  A pair
-  // doubles the bytes of its longest sequence's workgroup, so without the
-  // sum (no ragged split) that batch went from 76.4 to 95.9 us: pairs wait
-  // for the sum, and plans without it stay the pages' rule.
-  const bool pair = !dense && sum_seqlen_k > 0 && head_dim == 64 && hkv % 2 == 0 && pack &&
-                    int64_t(q_len) * 2 * group <= kBlockM;
+  // Head groups (paged, head_dim 64 or 32, packed, R = 128 / head_dim
+  // dividing the KV heads, all R heads' rows within one 16-row block, and
+  // the length sum given): R adjacent KV heads are one 128-wide key row in
+  // the cache, so a workgroup reads 256 contiguous bytes per key instead of
+  // 128 or 64, and 1/R as many workgroups move the same bytes.  Measured on
+  // MI355X: fp16 GQA-4 d 64, 64 sequences of 2048 keys, 53.7 -> 46.8 us;
+  // the ragged 128-sequence GQA-2 d-64 batch with its length sum, 54.0 ->
+  // 48.7 us; bf16 GQA-4 d 32, 32 sequences of 4096 keys, 46.4 -> 28.0 us
+  // (S 4: the quads leave 64 units, so the rule splits them).
+  // A group multiplies the bytes of its longest sequence's workgroup, so
+  // without the sum (no ragged split) the ragged batch went from 76.4 to
+  // 95.9 us: groups wait for the sum, and plans without it stay the pages'
+  // rule.
+  const int per_row = head_dim == 64 ? 2 : head_dim == 32 ? 4 : 1;
+  const bool grouped = !dense && sum_seqlen_k > 0 && per_row > 1 && hkv % per_row == 0 &&
+                       pack && int64_t(q_len) * per_row * group <= kBlockM;
+  const int64_t hr = grouped ? per_row : 1;  // KV heads per unit
   int splits = num_splits;
   if (splits == 0) {
-    const int64_t heads = pair ? hkv / 2 : pack ? hkv : hq;
-    const int64_t rows = pair ? int64_t(q_len) * 2 * group : pack ? int64_t(q_len) * group : q_len;
+    const int64_t heads = grouped ? hkv / hr : pack ? hkv : hq;
+    const int64_t rows =
+        grouped ? int64_t(q_len) * hr * group : pack ? int64_t(q_len) * group : q_len;
     const int64_t total = batch * heads * ceil_div(rows, kBlockM);
     splits = num_splits_rule(total, num_cus, ceil_div(max_seqlen_k, kBlockN));
     const int64_t rpb0 = rows_per_block(rows, head_dim);
@@ -154,10 +160,10 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   if (splits > 1) pack = true;  // same article, section "常见坑点"
 
   const int64_t rows_per_unit =
-      pair ? int64_t(q_len) * 2 * group : pack ? int64_t(q_len) * group : q_len;
-  const int rpb = rows_per_block(rows_per_unit, pair ? 2 * head_dim : head_dim);
+      grouped ? int64_t(q_len) * hr * group : pack ? int64_t(q_len) * group : q_len;
+  const int rpb = rows_per_block(rows_per_unit, grouped ? 128 : head_dim);
   const int64_t row_blocks = ceil_div(rows_per_unit, rpb);
-  const int64_t unit_heads = pair ? hkv / 2 : pack ? hkv : hq;
+  const int64_t unit_heads = grouped ? hkv / hr : pack ? hkv : hq;
   const int64_t units = batch * unit_heads * row_blocks;
   int64_t grid = units * splits;
   if (grid > INT32_MAX || rows_per_unit > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -198,8 +204,8 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
   out->split_granule = kGranule;
   out->num_cus = num_cus;
   out->combine = splits > 1 ? 2 : 0;
-  out->kernel = kernel_id(head_dim, !dense, pair);
-  out->head_pair = pair ? 1 : 0;
+  out->kernel = kernel_id(head_dim, !dense, grouped);
+  out->heads_per_row = int(hr);
   out->split_keys = int(split_keys);
   out->extra_blocks = int(extra);
   out->workspace_bytes = ws;
@@ -267,10 +273,10 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   prm.rows = plan.rows_per_unit;
   prm.row_blocks = plan.row_blocks;
   prm.nrb = plan.rows_per_block / kRowsPerBlock;
-  if (plan.head_pair) {  // a unit is a pair of adjacent KV heads
-    prm.head_pair = 1;
-    prm.hkv /= 2;
-    prm.group *= 2;
+  if (plan.heads_per_row > 1) {  // a unit is a group of adjacent KV heads
+    prm.head_group = plan.heads_per_row;
+    prm.hkv /= plan.heads_per_row;
+    prm.group *= plan.heads_per_row;
   }
   prm.heads_per_unit = plan.pack_gqa ? prm.group : 1;
   prm.unit_heads = plan.pack_gqa ? prm.hkv : prm.hq;

@@ -40,8 +40,9 @@ struct SplitParams {
   int n_si, n_sh;
   float scale_log2;    // softmax scale * log2(e)
   int by_length;       // paged: run sequences longest first (batch <= kMaxRankBatch)
-  int head_pair;       // paged, head_dim 64: a unit is two adjacent KV heads read as one
-                       // 128-wide key row (hkv, group and heads_per_unit count pairs)
+  int head_group;      // paged, head_dim 64 or 32, > 1: a unit is head_group adjacent KV
+                       // heads read as one 128-wide key row (hkv, group and
+                       // heads_per_unit count such groups)
   int extra_blocks;    // paged, 0: split-major grid of units * num_splits workgroups;
                        // > 0: extra_blocks workgroups take the splits >= 1 from a
                        // device-built list, then one workgroup per unit runs split 0

@@ -2,8 +2,8 @@
 //
 // Work unit: (sequence, head unit, block of 16, 32 or 64 packed query rows,
 // split).  A head unit is one KV head with its G query heads packed into the
-// rows (pack_gqa), one query head, or (head dim 64) a pair of adjacent KV
-// heads read as one 128-wide key row.  One workgroup per unit; its waves take the
+// rows (pack_gqa), one query head, or (head dims 64 and 32) 2 or 4
+// adjacent KV heads read as one 128-wide key row.  One workgroup per unit; its waves take the
 // 16-key tiles of the split's key range round-robin, each with its own online
 // softmax state, and merge through LDS at the end.  The two contractions run
 // on the matrix cores:
@@ -169,8 +169,8 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
 //   1  head_dim a multiple of 8 (rows stay 16-byte aligned): 16-byte loads,
 //      a chunk past the head dim gets an offset past the buffer range;
 //   2  any other head_dim: 16-bit element loads;
-//   3  head pairs (paged, D = 128, head_dim 64): 16-byte loads of whole
-//      128-wide rows of two adjacent KV heads.
+//   3  head groups (paged, D = 128, head_dim 64 or 32): 16-byte loads of
+//      whole 128-wide rows of 2 or 4 adjacent KV heads.
 // NRB: 16-row blocks a workgroup carries (1; 2 or 4 when a unit has more
 // than 16 or 32 packed rows, so its KV is read once for up to 64 rows).
 // tid: the thread index (passed in so that the compact list's loop can
@@ -198,19 +198,20 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   constexpr bool kDma = NBUF == 0;
   static_assert(!kDma || (kSwz && GEN != 2), "direct-to-LDS tiles need >= 8 16-byte chunks a row");
   static_assert(D % 32 == 0, "head_dim");
-  // GEN 3 (paged, head pairs): two adjacent KV heads of head dim D / 2 are
-  // one D-wide key row (the cache layout puts them side by side), and the
-  // unit packs both heads' query rows.  A row's D / 2 query values sit in
-  // its own head's half of the D columns and the other half is zero, so its
-  // scores see only its head's keys; its output is the same half of O.
-  constexpr bool kPair = GEN == 3;
-  static_assert(!kPair || (PAGED && NRB == 1), "head pairs: paged, one row block");
-  const int hd = GEN == 0 ? D : kPair ? D / 2 : p.head_dim;  // query / output row
-  const int kvd = GEN == 1 || GEN == 2 ? p.head_dim : D;     // key / value row
-  // first tile column of packed row pr's head (head pairs: the second half
-  // for the second head's G = heads_per_unit / 2 rows)
+  // GEN 3 (paged, head groups): R = D / head_dim adjacent KV heads (2 at
+  // head dim 64, 4 at 32) are one D-wide key row (the cache layout puts
+  // them side by side), and the unit packs all R heads' query rows.  A
+  // row's head_dim query values sit in its own head's slice of the D
+  // columns and the rest is zero, so its scores see only its head's keys;
+  // its output is the same slice of O.
+  constexpr bool kGroup = GEN == 3;
+  static_assert(!kGroup || (PAGED && NRB == 1 && D == 128), "head groups: paged, one row block");
+  const int hd = GEN == 0 ? D : p.head_dim;              // query / output row
+  const int kvd = GEN == 1 || GEN == 2 ? p.head_dim : D;  // key / value row
+  // first tile column of packed row pr's head (head groups: slice
+  // (pr mod R*G) / G of the row, G = heads_per_unit * head_dim / D)
   auto col0 = [&](int pr) {
-    return kPair ? ((pr % p.heads_per_unit) >= (p.heads_per_unit >> 1) ? D / 2 : 0) : 0;
+    return kGroup ? ((pr % p.heads_per_unit) / (p.heads_per_unit * hd / D)) * hd : 0;
   };
 
   struct Buf {
@@ -329,7 +330,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       }
     } else {
       const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd);
-      const int c0 = col0(rowq) / 8;  // first 16-byte chunk of this row's half (head pairs)
+      const int c0 = col0(rowq) / 8;  // first 16-byte chunk of this row's slice (head groups)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int c = chunk(g, kb) - c0;
@@ -876,9 +877,10 @@ hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
 template <int DT, bool PAGED>
 hipError_t launch_mfma_dt(const SplitParams& p, int grid, hipStream_t s) {
   const int d = p.head_dim;
-  if (p.head_pair) {  // two head-dim-64 KV heads per 128-wide tile
+  if (p.head_group > 1) {  // 2 head-dim-64 or 4 head-dim-32 KV heads per 128-wide row
     if constexpr (PAGED) {
-      if (d == 64 && p.nrb == 1) return launch_mfma_k<DT, 128, PAGED, 3, 1>(p, grid, s);
+      if (p.head_group * d == 128 && p.nrb == 1)
+        return launch_mfma_k<DT, 128, PAGED, 3, 1>(p, grid, s);
     }
     return hipErrorInvalidValue;
   }

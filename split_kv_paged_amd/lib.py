@@ -41,7 +41,7 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_splits", "pack_gqa", "rows_per_unit", "rows_per_block", "row_blocks", "units",
         "grid", "split_granule", "num_cus", "combine", "kernel", "split_keys",
-        "head_pair", "extra_blocks")] + [
+        "heads_per_row", "extra_blocks")] + [
         ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):

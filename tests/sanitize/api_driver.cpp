@@ -48,10 +48,12 @@ static void check_plan(const attn_plan& p, int64_t max_seqlen) {
         "grid = units * splits, or units + extra blocks");
   CHECK(p.extra_blocks == 0 || (p.num_splits > 1 && p.grid < int64_t(p.units) * p.num_splits),
         "a compact list only for a split call, and only when it is smaller");
-  CHECK(p.extra_blocks >= 0 && (p.head_pair == 0 || p.head_pair == 1), "plan flags");
-  CHECK(p.head_pair == 0 || (p.pack_gqa == 1 && p.rows_per_unit <= 16 && p.row_blocks == 1 &&
-                             p.kernel == 41128),
-        "head pairs: packed, one 16-row block, the pair kernel");
+  CHECK(p.extra_blocks >= 0 &&
+            (p.heads_per_row == 1 || p.heads_per_row == 2 || p.heads_per_row == 4),
+        "plan flags");
+  CHECK(p.heads_per_row == 1 || (p.pack_gqa == 1 && p.rows_per_unit <= 16 && p.row_blocks == 1 &&
+                                 p.kernel == 41128),
+        "head groups: packed, one 16-row block, the group kernel");
   CHECK(p.split_keys >= 16 && p.split_keys % 16 == 0, "split keys in granules");
   CHECK(int64_t(p.split_keys) * p.num_splits >= max_seqlen, "splits cover max_seqlen_k");
   CHECK(p.workspace_bytes >= 0, "workspace size");

@@ -131,36 +131,42 @@ def test_plan_fields_are_consistent(lib):
     assert plan.rows_per_unit == 2 and plan.units == 2 * 8
 
 
-@pytest.mark.parametrize("kw,pair", [
-    (dict(q_len=1, hq=8, hkv=2), 1),     # G 4: 8 rows per pair
-    (dict(q_len=2, hq=8, hkv=2), 1),     # 16 rows per pair: still one block
-    (dict(q_len=3, hq=8, hkv=2), 0),     # 24 rows: no pair
-    (dict(q_len=1, hq=16, hkv=2), 1),    # G 8: 16 rows
-    (dict(q_len=1, hq=32, hkv=2), 0),    # G 16: 32 rows
-    (dict(q_len=1, hq=6, hkv=3), 0),     # an odd number of KV heads
-    (dict(q_len=1, hq=8, hkv=8), 0),     # MHA decode is not packed (rule): no pair
-    (dict(q_len=1, hq=8, hkv=2, pack=0), 0),
-    (dict(q_len=1, hq=8, hkv=2, d=128), 0),
-    (dict(q_len=1, hq=8, hkv=2, d=96), 0),
+@pytest.mark.parametrize("kw,per_row", [
+    (dict(q_len=1, hq=8, hkv=2), 2),     # d 64, G 4: 8 rows per pair
+    (dict(q_len=2, hq=8, hkv=2), 2),     # 16 rows per pair: still one block
+    (dict(q_len=3, hq=8, hkv=2), 1),     # 24 rows: no pair
+    (dict(q_len=1, hq=16, hkv=2), 2),    # G 8: 16 rows
+    (dict(q_len=1, hq=32, hkv=2), 1),    # G 16: 32 rows
+    (dict(q_len=1, hq=6, hkv=3), 1),     # an odd number of KV heads
+    (dict(q_len=1, hq=8, hkv=8), 1),     # MHA decode is not packed (rule): no group
+    (dict(q_len=1, hq=8, hkv=2, pack=0), 1),
+    (dict(q_len=1, hq=8, hkv=2, d=128), 1),
+    (dict(q_len=1, hq=8, hkv=2, d=96), 1),
+    (dict(q_len=1, hq=16, hkv=4, d=32), 4),   # d 32, G 4: 16 rows per quad
+    (dict(q_len=1, hq=8, hkv=8, d=32, pack=1), 4),  # MHA packed: 4 rows per quad
+    (dict(q_len=1, hq=24, hkv=4, d=32), 1),   # G 6: 24 rows per quad
+    (dict(q_len=1, hq=12, hkv=6, d=32), 1),   # 6 KV heads: not a multiple of 4
+    (dict(q_len=2, hq=8, hkv=4, d=32), 4),    # q_len 2, G 2: 16 rows
 ])
-def test_head_pair_plan(lib, kw, pair):
-    """Paged head dim 64 with the length sum: two adjacent KV heads per unit
-    when the pair's packed rows fit one 16-row block; units, rows and the
-    split rule then count pairs.  Without the sum, no pairs."""
+def test_head_group_plan(lib, kw, per_row):
+    """Paged head dim 64 / 32 with the length sum: 2 / 4 adjacent KV heads
+    per unit when the group's packed rows fit one 16-row block; units, rows
+    and the split rule then count groups.  Without the sum, no groups."""
     kw = dict(kw)
     d = kw.pop("d", 64)
     code, plan = _plan(lib, batch=3, max_L=512, maxp=32, d=d, **kw)
-    assert code == 0 and plan.head_pair == 0
+    assert code == 0 and plan.heads_per_row == 1
     code, plan = _plan(lib, batch=3, max_L=512, maxp=32, d=d, sum_L=1200, **kw)
-    assert code == 0 and plan.head_pair == pair
+    assert code == 0 and plan.heads_per_row == per_row
     G = kw["hq"] // kw["hkv"]
-    if pair:
-        assert plan.pack_gqa == 1 and plan.rows_per_unit == kw["q_len"] * 2 * G
-        assert plan.units == 3 * (kw["hkv"] // 2) and plan.kernel == 41128
+    if per_row > 1:
+        assert plan.pack_gqa == 1 and plan.rows_per_unit == kw["q_len"] * per_row * G
+        assert plan.units == 3 * (kw["hkv"] // per_row) and plan.kernel == 41128
         assert plan.rows_per_block == 16 and plan.row_blocks == 1
-        # the split rule sees the pairs: the pages' rule with Hkv / 2 and 2G
-        want = oplan.plan(3, kw["q_len"], kw["hq"], kw["hkv"] // 2, 512, 256, 16, 128)
-        assert (plan.num_splits, bool(plan.pack_gqa)) == want
+        # the split rule sees the groups: the pages' rule with Hkv / R and R G
+        want = oplan.plan(3, kw["q_len"], kw["hq"], kw["hkv"] // per_row, 512, 256, 16, 128,
+                          0, kw.get("pack", -1))
+        assert plan.num_splits == want[0]
     # the workspace holds head_dim-wide partials of the real query rows
     code, plan = _plan(lib, batch=3, max_L=4096, maxp=256, d=d, S=3, sum_L=9000, **kw)
     nrows = 3 * kw["q_len"] * kw["hq"]
@@ -174,11 +180,11 @@ def test_plan_kernel_ids_name_the_tile_and_load_path(lib):
                     (1, 31032), (200, 21256), (33, 31064), (16, 21032), (130, 31256)]:
         code, plan = _plan(lib, batch=2, q_len=1, hq=8, hkv=2, max_L=512, maxp=32, d=d)
         assert code == 0 and plan.kernel == want, (d, plan.kernel)
-    # with the length sum, d 64 with two KV heads: a head pair on the 128-wide tile
+    # with the length sum, d 64 with two KV heads: a head group on the 128-wide tile
     code, plan = _plan(lib, batch=2, q_len=1, hq=8, hkv=2, max_L=512, maxp=32, d=64, sum_L=900)
-    assert code == 0 and plan.kernel == 41128 and plan.head_pair == 1
+    assert code == 0 and plan.kernel == 41128 and plan.heads_per_row == 2
     code, plan = _plan(lib, batch=2, q_len=1, hq=4, hkv=1, max_L=512, maxp=32, d=64, sum_L=900)
-    assert code == 0 and plan.kernel == 11064 and plan.head_pair == 0  # one KV head
+    assert code == 0 and plan.kernel == 11064 and plan.heads_per_row == 1  # one KV head
     shape = L.DenseShape(8, 2, 1, 512, 80, 0)
     plan = L.Plan()
     assert lib.attn_dense_plan(ctypes.byref(shape), 0, 0, ctypes.byref(plan)) == 0
@@ -338,7 +344,7 @@ def test_ragged_hint_plan(lib, name, kw, want):
     # without the hint the pages' rule alone decides
     kw0 = dict(kw, sum_L=0)
     code0, plan0 = _plan(lib, **kw0)
-    hkv = kw["hkv"] // 2 if plan0.head_pair else kw["hkv"]  # the rule counts head pairs
+    hkv = kw["hkv"] // plan0.heads_per_row  # the rule counts head groups
     ref_splits, _ = oplan.plan(kw["batch"], kw["q_len"], kw["hq"], hkv, kw["max_L"], 256, 16,
                                128)
     assert plan0.num_splits == ref_splits
@@ -374,7 +380,7 @@ def test_compact_list_plan(lib, name, kw, want):
     assert plan0.extra_blocks == 0 and plan0.grid == plan0.units * plan0.num_splits
     counters = lambda p: (p.units * 4 + 255) // 256 * 256 if p.num_splits > 1 else 0
     assert (plan0.workspace_bytes - counters(plan0)) == (plan.workspace_bytes - counters(plan))
-    assert plan0.units == plan.units * (2 if plan.head_pair else 1)
+    assert plan0.units == plan.units * plan.heads_per_row
     assert plan0.split_keys == plan.split_keys
     # a batch over 1024 sequences keeps the split-major grid
     if plan.num_splits > 1:

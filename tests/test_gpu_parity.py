@@ -469,27 +469,30 @@ def test_large_ragged_batch_unranked(length_sum):
             plan.num_splits, plan.extra_blocks, plan.grid, e1, e2), flush=True)
 
 
-PAIRS = [
-    # dtype, B, q_len, Hq, Hkv, lengths, causal, new_len, page size
-    ("fp16", 5, 1, 16, 8, [1, 17, 700, 2000, 64], False, 0, 16),    # G 2: 4 rows per pair
-    ("bf16", 4, 1, 32, 4, [300, 1025, 9, 4000], False, 0, 16),      # G 8: 16 rows
-    ("bf16", 3, 2, 16, 4, [500, 33, 1800], True, 0, 16),            # q_len 2, causal: 16 rows
-    ("fp16", 3, 1, 8, 2, [100, 2047, 5], False, 3, 16),             # keys appended first
-    ("bf16", 4, 1, 16, 4, [100, 1500, 47, 999], False, 0, 48),      # 48-key pages
+GROUPS = [
+    # dtype, B, q_len, Hq, Hkv, d, lengths, causal, new_len, page size
+    ("fp16", 5, 1, 16, 8, 64, [1, 17, 700, 2000, 64], False, 0, 16),   # G 2: 4 rows per pair
+    ("bf16", 4, 1, 32, 4, 64, [300, 1025, 9, 4000], False, 0, 16),     # G 8: 16 rows
+    ("bf16", 3, 2, 16, 4, 64, [500, 33, 1800], True, 0, 16),           # q_len 2, causal
+    ("fp16", 3, 1, 8, 2, 64, [100, 2047, 5], False, 3, 16),            # keys appended first
+    ("bf16", 4, 1, 16, 4, 64, [100, 1500, 47, 999], False, 0, 48),     # 48-key pages
+    ("bf16", 4, 1, 16, 4, 32, [1, 900, 3000, 47], False, 0, 16),       # d 32, G 4: a quad
+    ("fp16", 3, 2, 16, 8, 32, [700, 2, 1500], True, 0, 16),            # d 32, q_len 2, G 2
+    ("fp16", 3, 1, 8, 8, 32, [64, 2500, 33], False, 2, 16),            # d 32 MHA, appended
 ]
 
 
-@pytest.mark.parametrize("spec", PAIRS, ids=lambda c: "%s-B%d-q%d-G%d-new%d-P%d" % (
-    c[0], c[1], c[2], c[3] // c[4], c[7], c[8]))
+@pytest.mark.parametrize("spec", GROUPS, ids=lambda c: "%s-B%d-q%d-G%d-d%d-new%d-P%d" % (
+    c[0], c[1], c[2], c[3] // c[4], c[5], c[8], c[9]))
 @pytest.mark.parametrize("S", [1, 3])
-def test_head_pairs(spec, S):
-    """Head dim 64 with an even number of KV heads and the length sum: a
-    unit is a pair of adjacent KV heads on the 128-wide tile, each query row
-    in its head's half.  The output matches the oracle and, bit for bit, the unpacked
-    call (one query head per unit on the 64-wide tile): the pair only adds
-    exact zeros to each score."""
-    dt, B, qlen, hq, hkv, lens, causal, new_len, page = spec
-    d = 64
+def test_head_groups(spec, S):
+    """Head dim 64 / 32 with the length sum: a unit is 2 / 4 adjacent KV
+    heads on the 128-wide tile, each query row in its head's slice.  The
+    output matches the oracle and, bit for bit, the unpacked call (one query
+    head per unit on the head dim's own tile): the group only adds exact
+    zeros to each score."""
+    dt, B, qlen, hq, hkv, d, lens, causal, new_len, page = spec
+    R = 128 // d
     if new_len:
         assert page == 16
         wl, k_new, v_new, kc_h, vc_h = _append_case(1900 + B, dt, B, qlen, hq, hkv, d, lens,
@@ -507,24 +510,25 @@ def test_head_pairs(spec, S):
     kn = to_dev(k_new, dt) if new_len else None
     vn = to_dev(v_new, dt) if new_len else None
     got = {}
-    for pack in (-1, 0):
-        case("head pairs %s B%d q%d Hq%d/Hkv%d S=%d causal=%s new=%d pack=%d" % (
-            dt, B, qlen, hq, hkv, S, causal, new_len, pack))
+    for pack in ((1, 0) if hq == hkv else (-1, 0)):
+        case("head groups %s B%d q%d Hq%d/Hkv%d d%d S=%d causal=%s new=%d pack=%d" % (
+            dt, B, qlen, hq, hkv, d, S, causal, new_len, pack))
         out, lse = api.decode_fwd(q, kc, vc, bt, sl, num_splits=S, pack_gqa=pack,
                                   softmax_scale=wl.scale, max_seqlen_k=wl.max_seqlen_k,
                                   k_new=kn, v_new=vn, causal=causal,
                                   sum_seqlen_k=int(wl.cache_seqlens.sum()))
         torch.cuda.synchronize()
         plan = api.last_plan()
-        assert plan.head_pair == (1 if pack == -1 else 0)
+        assert plan.heads_per_row == (R if pack != 0 else 1)
         o, l = bits_of(out), lse.cpu().numpy()
         e1 = check_out(o, ref_o, dt)
         e2 = check_lse(l, ref_l)
-        print("  pair=%d units=%d max|dO|=%.3g max|dLSE|=%.3g" % (plan.head_pair, plan.units,
-                                                               e1, e2), flush=True)
+        print("  heads_per_row=%d units=%d max|dO|=%.3g max|dLSE|=%.3g" % (
+            plan.heads_per_row, plan.units, e1, e2), flush=True)
         got[pack] = (o, l)
-    assert np.array_equal(got[-1][0], got[0][0])
-    assert np.array_equal(got[-1][1], got[0][1], equal_nan=True)
+    grouped = got[1] if hq == hkv else got[-1]
+    assert np.array_equal(grouped[0], got[0][0])
+    assert np.array_equal(grouped[1], got[0][1], equal_nan=True)
 
 
 # ------------------------------------------------------------- varlen Q ----
@@ -572,10 +576,10 @@ def test_varlen_queries(shape, causal, S, length_sum):
     torch.cuda.synchronize()
     if length_sum:
         plan = api.last_plan()
-        print("  plan S=%d extra_blocks=%d head_pair=%d" % (
-            plan.num_splits, plan.extra_blocks, plan.head_pair), flush=True)
+        print("  plan S=%d extra_blocks=%d heads_per_row=%d" % (
+            plan.num_splits, plan.extra_blocks, plan.heads_per_row), flush=True)
         assert plan.extra_blocks > 0
-        assert plan.head_pair == (1 if (d == 64 and hq // hkv * maxq * 2 <= 16) else 0)
+        assert plan.heads_per_row == (2 if (d == 64 and hq // hkv * maxq * 2 <= 16) else 1)
     check_out(bits_of(out), ref_o, dt)
     check_lse(lse.cpu().numpy(), ref_l)
     assert api.last_plan().pack_gqa == 1
