@@ -70,7 +70,7 @@ int main() {
   const int batches[] = {0, 1, 7, 1024, 65536, 1 << 20};
   const int qlens[] = {1, 2, 8, 64, 4096};
   const int heads[][2] = {{1, 1}, {8, 2}, {32, 8}, {64, 1}, {128, 128}, {6, 4}};
-  const int dims[] = {1, 8, 64, 96, 128, 255, 256, 257};
+  const int dims[] = {1, 8, 32, 64, 96, 128, 255, 256, 257};
   const int pages[] = {16, 48, 17};
   const int lens[] = {0, 1, 1000, 16384, 1 << 20, 1 << 30};
   const int splits[] = {-1, 0, 1, 4, 1024, 1025};
