@@ -834,3 +834,30 @@ def test_seeded_mixture(k):
     torch.cuda.synchronize()
     check_out(bits_of(out), ref_o, dt)
     check_lse(lse.cpu().numpy(), ref_l)
+
+
+@pytest.mark.parametrize("k", range(24, 48))
+def test_seeded_mixture_with_length_sum(k):
+    """More of the seeded mixture, each call given its length sum, so the
+    plans also use the ragged split rule, the compact split list and head
+    groups where they apply (every other configuration takes head dim 32 or
+    64, where head groups exist)."""
+    dt, d, hkv, G, qlen, causal, B, lens, outl, S = _random_config(k)
+    if k % 2 == 0:
+        d = (32, 64)[(k // 2) % 2]
+    wl = W.make_paged(9100 + k, dt, B, qlen, hkv * G, hkv, d, 16, lens, spare_pages=1,
+                      outlier_p=outl)
+    case("mixture %d with the length sum: %s d%d Hkv%d G%d q%d causal=%s B%d L=%s "
+         "outliers=%g S=%d" % (k, dt, d, hkv, G, qlen, causal, B, lens, outl, S))
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    out, lse = api.decode_fwd(to_dev(wl.q, dt), to_dev(wl.k_cache, dt), to_dev(wl.v_cache, dt),
+                              i32_dev(wl.block_table), i32_dev(wl.cache_seqlens), num_splits=S,
+                              softmax_scale=wl.scale, max_seqlen_k=max(wl.max_seqlen_k, 0),
+                              causal=causal, sum_seqlen_k=int(sum(lens)))
+    torch.cuda.synchronize()
+    plan = api.last_plan()
+    e1 = check_out(bits_of(out), ref_o, dt)
+    e2 = check_lse(lse.cpu().numpy(), ref_l)
+    print("  plan S=%d heads_per_row=%d extra_blocks=%d max|dO|=%.3g max|dLSE|=%.3g" % (
+        plan.num_splits, plan.heads_per_row, plan.extra_blocks, e1, e2), flush=True)
