@@ -150,7 +150,8 @@ typedef struct {
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
     int32_t heads_per_row;   /* KV heads per unit: 1, or R = 2 (head_dim 64) */
                              /* or 4 (head_dim 32) when the call is paged,    */
-                             /* num_heads_kv is a multiple of R, packed,      */
+                             /* num_heads_kv is a multiple of R, packed (G = 1 */
+                             /* counts as packed unless pack_gqa is 0),        */
                              /* q_len * R * G <= 16 and sum_seqlen_k is       */
                              /* given: the R adjacent KV heads are read as    */
                              /* one 128-wide key row (the cache puts them     */

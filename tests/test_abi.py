@@ -138,7 +138,8 @@ def test_plan_fields_are_consistent(lib):
     (dict(q_len=1, hq=16, hkv=2), 2),    # G 8: 16 rows
     (dict(q_len=1, hq=32, hkv=2), 1),    # G 16: 32 rows
     (dict(q_len=1, hq=6, hkv=3), 1),     # an odd number of KV heads
-    (dict(q_len=1, hq=8, hkv=8), 1),     # MHA decode is not packed (rule): no group
+    (dict(q_len=1, hq=8, hkv=8), 2),     # MHA decode: the rule's no-pack changes no row
+    (dict(q_len=1, hq=8, hkv=8, pack=0), 1),  # unless packing is refused explicitly
     (dict(q_len=1, hq=8, hkv=2, pack=0), 1),
     (dict(q_len=1, hq=8, hkv=2, d=128), 1),
     (dict(q_len=1, hq=8, hkv=2, d=96), 1),
