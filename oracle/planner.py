@@ -22,8 +22,12 @@ from the prose of the lpnh.cn article "Flash-Attention GQA 性能调优：pack_g
 
 Readings (stated where the page is silent): the candidate range of split
 counts is 1 .. min(128, n_blocks); the unit count is
-batch * heads * ceil(rows / block_m) with heads = KV heads and
-rows = seqlen_q * G when packed, query heads and seqlen_q otherwise.
+batch * heads * ceil(rows / unit_block_m) with heads = KV heads and
+rows = seqlen_q * G when packed, query heads and seqlen_q otherwise.  The
+page's units are the kernel's thread blocks, each carrying one M tile of
+rows; where the kernel's block carries several MFMA tiles of rows,
+unit_block_m is the rows one block carries and block_m (the pack rule's
+tile) stays the MFMA tile.  unit_block_m defaults to block_m.
 """
 import math
 
@@ -69,12 +73,15 @@ def num_splits_heuristic(total_mblocks, num_sms, num_n_blocks, max_splits=MAX_SP
 
 
 def plan(batch, seqlen_q, num_heads_q, num_heads_kv, max_seqlen_k, num_sms, block_m, block_n,
-         num_splits=0, pack_gqa=-1, varlen_q=False):
+         num_splits=0, pack_gqa=-1, varlen_q=False, unit_block_m=None):
     """(num_splits, pack) for one call.
 
     num_splits: 0 = rule, else the caller's value.  pack_gqa: -1 = rule,
     0/1 = caller's value (still forced on when num_splits > 1).
+    unit_block_m: rows one thread block carries (default block_m), for the
+    unit count of the split rule.
     """
+    unit_m = block_m if unit_block_m is None else unit_block_m
     G = num_heads_q // num_heads_kv
     if pack_gqa < 0:
         pack = should_pack_gqa(varlen_q, seqlen_q, G, block_m)
@@ -83,7 +90,7 @@ def plan(batch, seqlen_q, num_heads_q, num_heads_kv, max_seqlen_k, num_sms, bloc
     if num_splits <= 0:
         heads = num_heads_kv if pack else num_heads_q
         rows = seqlen_q * G if pack else seqlen_q
-        total = batch * heads * ((rows + block_m - 1) // block_m)
+        total = batch * heads * ((rows + unit_m - 1) // unit_m)
         n_blocks = (max_seqlen_k + block_n - 1) // block_n
         splits = num_splits_heuristic(total, num_sms, n_blocks)
     else:

