@@ -126,7 +126,7 @@ typedef struct {
     int32_t num_splits;      /* S: KV ranges per (sequence, head unit)        */
     int32_t pack_gqa;        /* 1: the G query heads of a KV head share a unit */
     int32_t rows_per_unit;   /* query rows per unit: q_len*G packed, q_len not */
-                             /* (head pairs: q_len*2G)                         */
+                             /* (head groups of R KV heads: q_len*R*G)         */
     int32_t rows_per_block;  /* packed rows one workgroup carries: 16; at      */
                              /* head_dim 64 or 128, 32 for units of 17..32     */
                              /* rows and 64 beyond (KV read once per block)    */
