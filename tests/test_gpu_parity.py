@@ -722,18 +722,21 @@ def test_bitwise_determinism_and_page_permutation():
         assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
-@pytest.mark.parametrize("length_sum", [False, True], ids=["split-major", "compact"])
-def test_hip_graph_replays_match_eager(length_sum):
+@pytest.mark.parametrize("length_sum,d", [(False, 128), (True, 128), (True, 64)],
+                         ids=["split-major", "compact", "compact-head-pairs"])
+def test_hip_graph_replays_match_eager(length_sum, d):
     """A split call (fused combine, arrival counters rearmed by the kernel,
     no memset) captured in a HIP graph and replayed, with eager calls on
     other inputs in between: every replay equals the eager result.  With
-    the length sum the call launches the compact split list."""
-    wl = W.make_paged(1800, "bf16", 4, 2, 16, 4, 128, 16, [700, 33, 1500, 1], spare_pages=2)
+    the length sum the call launches the compact split list (and at head
+    dim 64 reads head pairs)."""
+    wl = W.make_paged(1800, "bf16", 4, 2, 16, 4, d, 16, [700, 33, 1500, 1], spare_pages=2)
     q, kc, vc = to_dev(wl.q, "bf16"), to_dev(wl.k_cache, "bf16"), to_dev(wl.v_cache, "bf16")
     bt, sl = i32_dev(wl.block_table), i32_dev(wl.cache_seqlens)
-    q2 = to_dev(W.make_paged(1801, "bf16", 4, 2, 16, 4, 128, 16, [700, 33, 1500, 1]).q, "bf16")
+    q2 = to_dev(W.make_paged(1801, "bf16", 4, 2, 16, 4, d, 16, [700, 33, 1500, 1]).q, "bf16")
     hint = int(wl.cache_seqlens.sum()) if length_sum else None
-    case("HIP graph capture of a 4-split decode call, 5 replays, length sum %s" % hint)
+    case("HIP graph capture of a 4-split decode call, d %d, 5 replays, length sum %s"
+         % (d, hint))
     call = api.PreparedDecode(q, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
                               max_seqlen_k=wl.max_seqlen_k, sum_seqlen_k=hint)
     other = api.PreparedDecode(q2, kc, vc, bt, sl, num_splits=4, softmax_scale=wl.scale,
@@ -741,6 +744,7 @@ def test_hip_graph_replays_match_eager(length_sum):
     call()
     torch.cuda.synchronize()
     assert (api.last_plan().extra_blocks > 0) == length_sum
+    assert api.last_plan().heads_per_row == (2 if (length_sum and d == 64) else 1)
     ref_o, ref_l = bits_of(call.out).copy(), call.lse.cpu().numpy().copy()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
