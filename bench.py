@@ -187,8 +187,9 @@ def main():
                   "kv_tokens": int(wl.cache_seqlens.sum()),
                   "length_sum_given": not args.no_length_sum}
     config.update({"kv_bytes": kv_bytes, "num_splits": last.num_splits,
-                   "pack_gqa": last.pack_gqa, "grid": last.grid, "kv_pools": len(pools),
-                   "accumulate": "f32"})
+                   "pack_gqa": last.pack_gqa, "heads_per_row": last.heads_per_row,
+                   "extra_blocks": last.extra_blocks, "grid": last.grid,
+                   "kv_pools": len(pools), "accumulate": "f32"})
 
     cpu = None
     if not args.no_cpu_baseline:
