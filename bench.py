@@ -160,7 +160,8 @@ def main():
     ceiling = None
     if not args.no_ceiling:
         ceiling = read_ceiling(wl, pools, None if dense else (bt, sl),
-                               last.split_keys if last.num_splits > 1 else 0, K, stream)
+                               last.split_keys if last.num_splits > 1 else 0, K, stream,
+                               last.heads_per_row)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -234,7 +235,7 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def read_ceiling(wl, pools, paged, split_keys, steps, stream):
+def read_ceiling(wl, pools, paged, split_keys, steps, stream, heads_per_row=1):
     """The empirical ceiling: read-only probes (libattn_probe.so) over the
     same KV bytes and pools as the timed calls, timed the same way (two
     events around `steps` back-to-back launches, pools rotated).
@@ -243,7 +244,9 @@ def read_ceiling(wl, pools, paged, split_keys, steps, stream):
                         contiguous, 512 workgroups
       page_gather_read  (paged) the valid keys' K and V rows, walked as the
                         decode kernel walks them (split as the timed calls
-                        were), with no arithmetic"""
+                        were, and with the calls' head groups read as one
+                        wider row: the same bytes viewed as num_heads_kv / R
+                        heads of R * head_dim), with no arithmetic"""
     import torch
     from split_kv_paged_amd import probe
 
@@ -270,12 +273,19 @@ def read_ceiling(wl, pools, paged, split_keys, steps, stream):
     res = {"stream_read": entry(2 * half, timed(calls))}
     if paged is not None:
         bt, sl = paged
-        first, psums = probe.prepared_page_read(pools[0][0], pools[0][1], bt, sl,
+        R = max(1, heads_per_row)
+
+        def view(t):  # R adjacent KV heads as one row of R * head_dim
+            n, page, hkv, d = t.shape
+            return t.view(n, page, hkv // R, R * d)
+        first, psums = probe.prepared_page_read(view(pools[0][0]), view(pools[0][1]), bt, sl,
                                                 wl.max_seqlen_k, split_keys, None, stream)
-        calls = [first] + [probe.prepared_page_read(k, v, bt, sl, wl.max_seqlen_k, split_keys,
-                                                    psums, stream)[0] for k, v in pools[1:]]
+        calls = [first] + [probe.prepared_page_read(view(k), view(v), bt, sl, wl.max_seqlen_k,
+                                                    split_keys, psums, stream)[0]
+                           for k, v in pools[1:]]
         res["page_gather_read"] = entry(wl.kv_bytes, timed(calls))
         res["page_gather_read"]["split_keys"] = split_keys
+        res["page_gather_read"]["heads_per_row"] = R
     res["method"] = "read-only probes over the same KV bytes and pools, events around %d " \
                     "back-to-back launches" % steps
     return res
