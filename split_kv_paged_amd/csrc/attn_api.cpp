@@ -277,7 +277,7 @@ attn_status check_workspace(const attn_plan& plan, void* ws, size_t ws_bytes) {
 
 // Launch the split kernel (which merges the splits itself when S > 1).
 attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dtype, int head_dim,
-                void* out, float* lse, void* ws, hipStream_t stream) {
+                void* out, float* lse, void* ws, hipStream_t stream, int64_t max_seqlen_k = 0) {
   const int S = plan.num_splits;
   prm.num_splits = S;
   prm.split_keys = plan.split_keys;
@@ -303,7 +303,8 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   }
   // Paged calls whose grid needs more than one round run the first split's
   // sequences longest first (ranked inside its workgroups).
-  prm.by_length = paged && prm.batch <= skv::kMaxRankBatch && plan.grid > plan.num_cus;
+  prm.by_length = paged && prm.batch <= skv::kMaxRankBatch && plan.grid > plan.num_cus &&
+                  max_seqlen_k >= skv::kMinRankKeys;
   prm.extra_blocks = paged ? plan.extra_blocks : 0;
   if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream) != hipSuccess)
     return ATTN_ERR_HIP;
@@ -389,7 +390,8 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
     a.max_pages = shape->max_pages_per_seq;
     if (skv::launch_append(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
   }
-  return run(plan, p, true, shape->dtype, D, out, lse, workspace, static_cast<hipStream_t>(stream));
+  return run(plan, p, true, shape->dtype, D, out, lse, workspace, static_cast<hipStream_t>(stream),
+             shape->max_seqlen_k);
 }
 
 }  // namespace

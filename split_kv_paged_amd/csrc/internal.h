@@ -39,7 +39,7 @@ struct SplitParams {
   int nrows;           // batch * q_len * Hq
   int n_si, n_sh;
   float scale_log2;    // softmax scale * log2(e)
-  int by_length;       // paged: run sequences longest first (batch <= kMaxRankBatch)
+  int by_length;       // paged: run sequences longest first (see kMaxRankBatch)
   int head_group;      // paged, head_dim 64 or 32, > 1: a unit is head_group adjacent KV
                        // heads read as one 128-wide key row (hkv, group and
                        // heads_per_unit count such groups)
@@ -68,12 +68,19 @@ struct AppendParams {
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
 constexpr int kMaxOrderBatch = 1024;  // largest batch of the compact split list (its LDS list)
-// Largest batch whose split-0 workgroups rank the sequences by length.  The
-// ranking is O(batch^2) per workgroup: measured on MI355X (paged, 8 KV
-// heads), 128 ragged sequences d 64 run 53.9 us ranked against 61.3
-// unranked, 64 of them 30.1 against 35.3; 256 sequences of 100..300 keys
-// 65.7 against 43.5, and 1024 of them 1199 against 159.
-constexpr int kMaxRankBatch = 128;
+// Split-0 workgroups rank the sequences by length (longest first) for
+// batches of at most kMaxRankBatch sequences whose longest has at least
+// kMinRankKeys keys.  Each workgroup pays a round trip for the lengths and
+// an O(batch^2 / threads) count, which only pays where the order matters.
+// Measured on MI355X (paged, 8 KV heads; ranked / unranked, us): 128
+// sequences of 100..300 keys 26.3 / 24.2 and of 500..1500 keys 88.2 / 94.9;
+// 128 ragged sequences (1..8192 keys) 75.0 / 91.4, with their length sum
+// 48.7 / 57.7; 64 ragged ones (1..4096) 29.7 / 35.8; 256 ragged ones with
+// their sum 97.9 / 106.5; 256 of 100..300 keys 64.8 / 43.0; 512 ragged ones
+// (1..4096) 189 / 125.
+constexpr int kMaxRankBatch = 256;
+constexpr int kMinRankKeys = 1024;
+static_assert(kMaxRankBatch % 16 == 0 && kMaxRankBatch <= kMaxOrderBatch, "rank list size");
 
 struct CombineParams {
   const float* o_part;

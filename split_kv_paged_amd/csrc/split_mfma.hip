@@ -728,10 +728,11 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 // short sequences are never launched.  The host sizes extra_blocks from the
 // length sum so that each takes one item; with a smaller count (a wrong
 // sum) they loop over the items, which stays correct.
-// In both, when the grid takes more than one round of workgroups and the
-// batch is small (kMaxRankBatch), split 0 (the one every sequence has) runs
-// its sequences longest first (a longest-processing-time order): each of
-// its workgroups ranks the batch by length, ties by index.
+// In both, when the grid takes more than one round of workgroups, the
+// batch is small (kMaxRankBatch) and its sequences long (kMinRankKeys),
+// split 0 (the one every sequence has) runs its sequences longest first (a
+// longest-processing-time order): each of its workgroups ranks the batch
+// by length, ties by index.
 // The row blocks of one (sequence, head unit) sit 8 workgroups apart:
 // workgroups are dealt to the 8 XCDs round-robin, so they land on the same
 // XCD, close in time, and the second one to read a KV tile finds it in
@@ -743,7 +744,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB, bool EXTRA>
 __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
   static_assert(PAGED || !EXTRA, "the compact list is for paged calls");
-  __shared__ int s_seq[kMaxOrderBatch + 1];
+  __shared__ __attribute__((aligned(16))) int s_seq[kMaxOrderBatch + 1];
   if (EXTRA && int(blockIdx.x) < p.extra_blocks) {
     // Extra items of sequence b: (n_b - 1) x head units x row blocks, with
     // n_b = ceil(L_b / split_keys) splits (at most num_splits, as in the
@@ -814,18 +815,30 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   const int uh = bid % p.unit_heads;
   int b = bid / p.unit_heads;
   if (PAGED && p.by_length && split == 0) {
+    // Rank of sequence i: the sequences longer than it, plus the equally
+    // long ones before it.  Four adjacent threads share a sequence, each
+    // comparing a quarter of the batch 4 lengths per LDS read (lengths
+    // padded to a multiple of 16 with -1, below every real length), and
+    // add their counts with two shuffles.
     int* const s_len = s_seq;
     __shared__ int s_pick;
-    for (int i = threadIdx.x; i < p.batch; i += NW * 64) s_len[i] = p.seqlens[i];
+    const int bp = (p.batch + 15) & ~15;  // <= kMaxRankBatch <= kMaxOrderBatch
+    for (int i = threadIdx.x; i < bp; i += NW * 64) s_len[i] = i < p.batch ? max(p.seqlens[i], 0) : -1;
     __syncthreads();
-    for (int i = threadIdx.x; i < p.batch; i += NW * 64) {
-      const int li = s_len[i];
+    const int q = threadIdx.x & 3;
+    const int quarter = bp >> 2;  // a multiple of 4
+    for (int i0 = 0; i0 < p.batch; i0 += NW * 16) {
+      const int i = i0 + int(threadIdx.x >> 2);
+      const int li = s_len[min(i, bp - 1)];
       int rank = 0;
-      for (int j = 0; j < p.batch; ++j) {
-        const int lj = s_len[j];
-        rank += (lj > li) || (lj == li && j < i);
+      for (int j = q * quarter; j < (q + 1) * quarter; j += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(s_len + j);
+        rank += (v.x > li) + (v.x == li && j < i) + (v.y > li) + (v.y == li && j + 1 < i) +
+                (v.z > li) + (v.z == li && j + 2 < i) + (v.w > li) + (v.w == li && j + 3 < i);
       }
-      if (rank == b) s_pick = i;
+      rank += __shfl_xor(rank, 1);
+      rank += __shfl_xor(rank, 2);
+      if (q == 0 && i < p.batch && rank == b) s_pick = i;
     }
     __syncthreads();
     b = __builtin_amdgcn_readfirstlane(s_pick);
