@@ -246,6 +246,27 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   const int rows_b = p.cu_q ? qlen_b * p.heads_per_unit : p.rows;  // real packed rows
   const int row0 = rb * 16 * NRB;  // first packed row of this workgroup
   if (row0 >= rows_b) return;      // a row block past this sequence's queries
+  // The page ids of the first tiles and the query rows do not depend on the
+  // sequence's length: their loads go out together with the length load, so
+  // the first tile waits for one round trip instead of two.
+  int pages = load_pages(0);
+  auto row_of = [&](int i, int hq) -> long {
+    return (long)(qbase + i) * p.n_si + (long)hq * p.n_sh;
+  };
+  auto lse_of = [&](int i, int hq) -> long {
+    return p.cu_q ? (long)hq * p.total_q + qbase + i : ((long)b * p.hq + hq) * p.q_len + i;
+  };
+  // ---- Q^T as the B operand: lane l holds row l%16 of each 16-row block,
+  // chunks g*KB + kb ------------------------------------------------------
+  // Four row blocks at D = 128 would need 64 more VGPRs than eight waves
+  // have next to their accumulators, so there the workgroup stages its 64
+  // query rows in LDS and each wave reads a row block's operand per tile.
+  // Otherwise each lane loads its rows' operands into registers, after the
+  // first tile has gone out (the loads then overlap the tile's flight, and
+  // the first tile waits for the page ids alone).
+  constexpr bool kQLds = NRB == 4 && D == 128;
+  static_assert(!kQLds || GEN == 0, "staged Q rows are whole 16-byte chunks");
+  uint4 qb[kQLds ? 1 : NRB][KB];
   const int L = PAGED ? p.seqlens[b] + p.seq_add : p.kv_len;
   // Splits of this sequence that hold keys.  Past the last key a split has
   // nothing to add (its LSE would be -inf, weight zero in the combine), so
@@ -254,13 +275,10 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   const int nsplit = p.num_splits == 1 ? 1 : max(1, (L + p.split_keys - 1) / p.split_keys);
   if (split >= nsplit) return;
   const bool direct = nsplit == 1;
-  int pages = load_pages(0);
   const int t1 = min(t0 + p.split_keys, L);
   const int n_tiles = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
-  // ---- Q^T as the B operand: lane l holds row l%16 of each 16-row block,
-  // chunks g*KB + kb ------------------------------------------------------
   // Keys a lane's row may see: [t0, lim[r]).  Causal (bottom-right): query
   // i of q_len sees keys j <= L - q_len + i.  Every tile applies the mask
   // (a few VALU ops); a separate unmasked copy of the tile code would make
@@ -275,18 +293,6 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       lim[r] = min(t1, max(0, L - qlen_b + 1 + i_row));
     }
   }
-  auto row_of = [&](int i, int hq) -> long {
-    return (long)(qbase + i) * p.n_si + (long)hq * p.n_sh;
-  };
-  auto lse_of = [&](int i, int hq) -> long {
-    return p.cu_q ? (long)hq * p.total_q + qbase + i : ((long)b * p.hq + hq) * p.q_len + i;
-  };
-  // Q^T operands.  Four row blocks at D = 128 would need 64 more VGPRs than
-  // eight waves have next to their accumulators, so there the workgroup
-  // stages its 64 query rows in LDS once (16-byte chunks of row r at
-  // c ^ f(r), as for K) and each wave reads a row block's operand per tile.
-  constexpr bool kQLds = NRB == 4 && D == 128;
-  static_assert(!kQLds || GEN == 0, "staged Q rows are whole 16-byte chunks");
   __shared__ __attribute__((aligned(16))) uint8_t s_q[kQLds ? 16 * NRB * D * 2 : 16];
   if constexpr (kQLds) {
     constexpr int kChunks = 16 * NRB * (D / 8);  // 16-byte chunks of the 64 rows
@@ -302,41 +308,6 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       *reinterpret_cast<uint4*>(s_q + rr * (D * 2) + ((cc ^ f) * 16)) = v;
     }
     __syncthreads();
-  }
-  uint4 qb[kQLds ? 1 : NRB][KB];
-#pragma unroll
-  for (int r = 0; r < (kQLds ? 0 : NRB); ++r) {
-    const int rowq = row0 + 16 * r + n16;  // packed row of this lane in block r of S^T
-    bool real = rowq < rows_b;
-    long n = 0;
-    if (real) {
-      const int i = rowq / p.heads_per_unit;
-      const int hq = hq0 + rowq % p.heads_per_unit;
-      n = row_of(i, hq);
-    }
-    if constexpr (GEN == 2) {
-      const uint16_t* qr = static_cast<const uint16_t*>(p.q) + n * hd;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c0 = chunk(g, kb) * 8 + 2 * e;
-          const uint32_t lo = (real && c0 < hd) ? qr[c0] : 0u;
-          const uint32_t hi = (real && c0 + 1 < hd) ? qr[c0 + 1] : 0u;
-          w[e] = lo | (hi << 16);
-        }
-        qb[r][kb] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    } else {
-      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd);
-      const int c0 = col0(rowq) / 8;  // first 16-byte chunk of this row's slice (head groups)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int c = chunk(g, kb) - c0;
-        qb[r][kb] = (real && c >= 0 && (GEN == 0 || c * 8 < hd)) ? qp[c] : make_uint4(0, 0, 0, 0);
-      }
-    }
   }
 
   f4_t acc[NRB][DB];  // O blocks
@@ -420,6 +391,42 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
     }
   };
 
+  auto load_q = [&]() {
+#pragma unroll
+    for (int r = 0; r < (kQLds ? 0 : NRB); ++r) {
+      const int rowq = row0 + 16 * r + n16;  // packed row of this lane in block r of S^T
+      const bool real = rowq < rows_b;
+      long n = 0;
+      if (real) {
+        const int i = rowq / p.heads_per_unit;
+        const int hq = hq0 + rowq % p.heads_per_unit;
+        n = row_of(i, hq);
+      }
+      if constexpr (GEN == 2) {
+        const uint16_t* qr = static_cast<const uint16_t*>(p.q) + n * hd;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c0 = chunk(g, kb) * 8 + 2 * e;
+            const uint32_t lo = (real && c0 < hd) ? qr[c0] : 0u;
+            const uint32_t hi = (real && c0 + 1 < hd) ? qr[c0 + 1] : 0u;
+            w[e] = lo | (hi << 16);
+          }
+          qb[r][kb] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      } else {
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd);
+        const int c0 = col0(rowq) / 8;  // first 16-byte chunk of this row's slice (head groups)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int c = chunk(g, kb) - c0;
+          qb[r][kb] = (real && c >= 0 && (GEN == 0 || c * 8 < hd)) ? qp[c] : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
   const float c = p.scale_log2;
   // A 16-bit probability rounded once has a relative error up to 2^-9
   // (bfloat16) or 2^-12 (fp16); times large, cancelling V rows that can
@@ -540,11 +547,17 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   if constexpr (kDma) {
     // s_waitcnt immediates: vmcnt(0) alone, lgkmcnt(0) alone
     constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
+    // The first tile goes out before the loop: there the compiler waits for
+    // the page ids alone, not for the query rows loaded after them.
+    if (my_tiles > 0) issue_dma(0, __builtin_amdgcn_readlane(pages, 0));
+    load_q();
     for (int cb = 0; cb < my_tiles; cb += 64) {
-      if (cb > 0) pages = load_pages(cb);
-      const int n = min(64, my_tiles - cb);
       auto page_at = [&](int i) { return __builtin_amdgcn_readlane(pages, i); };
-      issue_dma(cb, page_at(0));
+      if (cb > 0) {
+        pages = load_pages(cb);
+        issue_dma(cb, page_at(0));
+      }
+      const int n = min(64, my_tiles - cb);
       for (int i = 0; i < n; ++i) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);  // tile i has landed in the slot
         uint4 kq[KB];
@@ -560,6 +573,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       }
     }
   } else {  // NBUF tiles in a register ring
+  load_q();
   for (int cb = 0; cb < my_tiles; cb += 64) {
     if (cb > 0) pages = load_pages(cb);
     const int n = min(64, my_tiles - cb);
@@ -601,7 +615,12 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   for (int blk = 0; blk < NRB; ++blk) {
     const int rows_here = min(RMAX, rows_b - row0 - 16 * blk);
     if (rows_here <= 0) break;
-    __syncthreads();  // the V staging area (or the previous block) is reused below
+    // The merge rows reuse the tile slots.  With direct-to-LDS tiles, wave
+    // w's rows of the first block (16 x D floats) occupy exactly its own
+    // slot (16 K and 16 V rows of D 16-bit values), which it has read out,
+    // so only a later block (or a register-ring kernel, whose slots are
+    // smaller) waits for the other waves first.
+    if (!kDma || blk > 0) __syncthreads();
     const float l32b = across_rows<false>(l32[blk]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
