@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 typedef enum {
     ATTN_OK = 0,
@@ -193,7 +193,9 @@ attn_status attn_decode_plan(const attn_decode_shape* shape, int num_splits, int
  *     Layout: float32 partial outputs [S][rows][head_dim], then (at the
  *     next 256-byte boundary) float32 partial LSEs [S][rows], rows ordered
  *     (b, i, hq), then (next 256-byte boundary) int32 arrival counters
- *     [plan.units].  The counters must be zero before the first call that
+ *     [plan.units], one per 128-byte line (32 int32 apart, so the atomics
+ *     of different units never share a line).  The counters must be zero
+ *     before the first call that
  *     uses the workspace (fill it with zeros once); every call leaves them
  *     zero again.  Calls that share one workspace must not run concurrently.
  *     Only the partials of splits that hold keys of a sequence spanning two

@@ -201,7 +201,8 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
     // the fused combine addresses the partials with 32-bit byte offsets
     if (int64_t(splits) * nrows * head_dim * 4 >= (int64_t(1) << 32)) return ATTN_ERR_UNSUPPORTED;
     ws = round_up(int64_t(splits) * nrows * head_dim * 4, 256) +
-         round_up(int64_t(splits) * nrows * 4, 256) + round_up(units * 4, 256);
+         round_up(int64_t(splits) * nrows * 4, 256) +
+         round_up(units * 4 * skv::kCounterStride, 256);
   }
 
   std::memset(out, 0, sizeof(*out));

@@ -25,7 +25,8 @@ struct SplitParams {
   float* lse;                  // final LSE, may be null (num_splits == 1)
   float* o_part;               // [S][nrows][D] (num_splits > 1)
   float* lse_part;             // [S][nrows]    (num_splits > 1)
-  int* counters;               // [units] arrival counters, zero between calls (fused combine)
+  int* counters;               // [units] arrival counters (kCounterStride apart), zero between
+                               // calls (fused combine)
   int batch, q_len, hq, hkv, group;  // group = Hq / Hkv
   int page_size, max_pages, kv_len;
   int head_dim;        // elements per row of q, k, v and out
@@ -67,6 +68,9 @@ struct AppendParams {
 };
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
+// Arrival counters of the fused combine sit one per 128-byte line: the
+// atomics of different units then never queue on one line.
+constexpr int kCounterStride = 32;  // int32 elements between two units' counters
 constexpr int kMaxOrderBatch = 1024;  // largest batch of the compact split list (its LDS list)
 // Split-0 workgroups rank the sequences by length (longest first) for
 // batches of at most kMaxRankBatch sequences whose longest has at least

@@ -66,6 +66,7 @@ typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u4_t __attribute__((ext_vector_type(4)));
 
 template <int DT>
 struct Mf;
@@ -137,6 +138,14 @@ constexpr int kSysCoherent = 17;  // CPol::SC0 | CPol::SC1
 __device__ __forceinline__ void publish(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, int(byte_off), 0,
                                         kSysCoherent);
+}
+__device__ __forceinline__ void publish4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), r, int(byte_off), 0,
+                                         kSysCoherent);
+}
+__device__ __forceinline__ f4_t fetch4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, kSysCoherent));
 }
 __device__ __forceinline__ float fetch(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float,
@@ -606,11 +615,17 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 
   // ---- merge the waves through LDS and write, one 16-row block at a time --
   // O layout: lane l holds rows 4g..4g+3, columns 16db + n16.  m and the
-  // probability sum of row r are held by lanes with n16 == r.
+  // probability sum of row r are held by lanes with n16 == r.  Each row's
+  // weights are computed once: wave w's partial enters row r with weight
+  // 2^(m_w - M) / sum_w' 2^(m_w' - M) l_w' (M = max_w m_w), so an output
+  // element is a plain weighted sum over the waves, VEC columns per thread.
   constexpr int RMAX = 16;
+  constexpr int VEC = GEN == 2 ? 1 : 4;  // head dims of the 16-byte kernels are multiples of 8
   float* s_acc = reinterpret_cast<float*>(s_buf);  // [NW][16][D]
   __shared__ float s_m[NW][RMAX];
   __shared__ float s_l32[NW][RMAX];  // float32 probability sums
+  __shared__ float s_wt[NW][RMAX];   // weight of wave w's partial in row r
+  __shared__ float s_lse[RMAX];      // natural-log LSE of row r (-inf: no key)
 #pragma unroll
   for (int blk = 0; blk < NRB; ++blk) {
     const int rows_here = min(RMAX, rows_b - row0 - 16 * blk);
@@ -636,35 +651,58 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       s_l32[wave][n16] = l32b;
     }
     __syncthreads();
-
-    for (int t = tid; t < rows_here * hd; t += NW * 64) {
+    if (tid < NW * rows_here) {  // NW adjacent lanes per row, one per wave
+      const int w = tid % NW, r = tid / NW;
+      const float mw = s_m[w][r];
+      float mx = mw;
+#pragma unroll
+      for (int o = 1; o < NW; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - mx);
+      float den = f * s_l32[w][r];
+#pragma unroll
+      for (int o = 1; o < NW; o <<= 1) den += __shfl_xor(den, o);
+      const bool empty = mx == -INFINITY;  // no wave saw a key of this row
+      s_wt[w][r] = empty ? 0.f : f / den;
+      if (w == 0) s_lse[r] = empty ? -INFINITY : (mx + log2f(den)) * kLn2;
+    }
+    __syncthreads();
+    for (int t = tid * VEC; t < rows_here * hd; t += NW * 64 * VEC) {
       const int r = t / hd;
-      const int d = t % hd;
+      const int d = t % hd;  // a multiple of VEC, and VEC divides hd
       const int pr = row0 + 16 * blk + r;
       const int col = col0(pr) + d;
-      float Mx = -INFINITY;
+      float o[VEC];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][r]);
-      float num = 0.f, den = 0.f;
-      if (Mx != -INFINITY) {
+      for (int e = 0; e < VEC; ++e) o[e] = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const float f = (s_m[w][r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - Mx);
-          num = fmaf(f, s_acc[((long)w * RMAX + r) * D + col], num);
-          den = fmaf(f, s_l32[w][r], den);
+      for (int w = 0; w < NW; ++w) {
+        const float wt = s_wt[w][r];
+        const float* a = s_acc + ((long)w * RMAX + r) * D + col;
+        if constexpr (VEC == 4) {
+          const f4_t v = *reinterpret_cast<const f4_t*>(a);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = fmaf(wt, v[e], o[e]);
+        } else {
+          o[0] = fmaf(wt, a[0], o[0]);
         }
       }
-      const float o = (Mx == -INFINITY) ? 0.f : num / den;
-      const float lse = (Mx == -INFINITY) ? -INFINITY : (Mx + log2f(den)) * kLn2;
       const int i = pr / p.heads_per_unit;
       const int hq = hq0 + pr % p.heads_per_unit;
       const long nrow = row_of(i, hq);
       if (direct) {
-        static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(o);
-        if (d == 0 && p.lse) p.lse[lse_of(i, hq)] = lse;
+        uint16_t* dst = static_cast<uint16_t*>(p.out) + nrow * hd + d;
+        if constexpr (VEC == 4)
+          *reinterpret_cast<uint2*>(dst) = make_uint2(M::pack(o[0], o[1]), M::pack(o[2], o[3]));
+        else
+          dst[0] = M::round(o[0]);
+        if (d == 0 && p.lse) p.lse[lse_of(i, hq)] = s_lse[r];
       } else {  // write-through stores: the merging workgroup may sit on another XCD
-        publish(r_opart, uint32_t(((long)split * p.nrows + nrow) * hd + d) * 4u, o);
-        if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, lse);
+        const uint32_t off = uint32_t(((long)split * p.nrows + nrow) * hd + d) * 4u;
+        if constexpr (VEC == 4)
+          publish4(r_opart, off, (f4_t){o[0], o[1], o[2], o[3]});
+        else
+          publish(r_opart, off, o[0]);
+        if (d == 0) publish(r_lpart, uint32_t((long)split * p.nrows + nrow) * 4u, s_lse[r]);
       }
     }
   }
@@ -674,40 +712,52 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   // Every split that holds keys writes its partials through to memory
   // (system-coherent stores, no cache maintenance), waits until they are
   // complete, then bumps the unit's arrival counter; the workgroup that sees
-  // the other nsplit-1 arrivals before
-  // its own reads the partials back with cache-bypassing loads and merges
-  // them, writes the output and rearms the counter at zero for the next call.
-  // Each thread owns output elements and reads the partial LSE and O of
-  // kBatch splits in one round of independent loads, folding batches with
-  // the max-shifted log-sum-exp rule (running maximum, rescaled sums).
-  constexpr int kBatch = 16;
+  // the other nsplit-1 arrivals before its own reads the partials back with
+  // cache-bypassing loads and merges them, writes the output and rearms the
+  // counter at zero for the next call.
+  // Each thread owns VEC adjacent output columns of a row.  It reads the
+  // partial LSE and the VEC partial outputs (one 16-byte load) of kBatch
+  // splits in one round of independent loads and folds each batch with the
+  // max-shifted log-sum-exp rule (running maximum, rescaled sums); the
+  // lanes of a row load the same LSE addresses, which a wave's load
+  // coalesces.
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int kBatch = 16;
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
   __syncthreads();
   const int unit = (b * p.unit_heads + uh) * p.row_blocks + rb;
+  int* const counter = p.counters + (long)unit * kCounterStride;
   if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_SYSTEM) == nsplit - 1;
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+             nsplit - 1;
   __syncthreads();
   if (!s_last) return;
   const int S = nsplit;
   const int rows_unit = min(16 * NRB, rows_b - row0);
-  for (int t = tid; t < rows_unit * hd; t += NW * 64) {
+  for (int t = tid * VEC; t < rows_unit * hd; t += NW * 64 * VEC) {
     const int r = t / hd;
     const int d = t % hd;
     const int pr = row0 + r;
     const int i = pr / p.heads_per_unit;
     const int hq = hq0 + pr % p.heads_per_unit;
     const long nrow = row_of(i, hq);
-    float mx = -INFINITY, wsum = 0.f, acc_o = 0.f;  // log2 units
+    float mx = -INFINITY, wsum = 0.f;  // log2 units
+    float acc_o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc_o[e] = 0.f;
     for (int sp0 = 0; sp0 < S; sp0 += kBatch) {
-      float ls[kBatch], o[kBatch];
+      float ls[kBatch];
+      f4_t o[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {  // unconditional loads (clamped index), no branches
         const int sp = min(sp0 + k, S - 1);
         ls[k] = fetch(r_lpart, uint32_t((long)sp * p.nrows + nrow) * 4u);
-        o[k] = fetch(r_opart, uint32_t(((long)sp * p.nrows + nrow) * hd + d) * 4u);
+        const uint32_t off = uint32_t(((long)sp * p.nrows + nrow) * hd + d) * 4u;
+        if constexpr (VEC == 4)
+          o[k] = fetch4(r_opart, off);
+        else
+          o[k][0] = fetch(r_opart, off);
       }
       float bm = -INFINITY;
 #pragma unroll
@@ -718,21 +768,28 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       const float mn = fmaxf(mx, bm);  // stays -inf while no split had keys
       const float alpha = mx == mn ? 1.f : fast_exp2(mx - mn);
       wsum *= alpha;
-      acc_o *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc_o[e] *= alpha;
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         const float w = ls[k] == -INFINITY ? 0.f : fast_exp2(ls[k] - mn);
         wsum += w;
-        acc_o = fmaf(w, o[k], acc_o);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc_o[e] = fmaf(w, o[k][e], acc_o[e]);
       }
       mx = mn;
     }
-    static_cast<uint16_t*>(p.out)[nrow * hd + d] = M::round(mx == -INFINITY ? 0.f : acc_o / wsum);
+    const float inv = mx == -INFINITY ? 0.f : 1.f / wsum;
+    uint16_t* dst = static_cast<uint16_t*>(p.out) + nrow * hd + d;
+    if constexpr (VEC == 4)
+      *reinterpret_cast<uint2*>(dst) = make_uint2(M::pack(acc_o[0] * inv, acc_o[1] * inv),
+                                                  M::pack(acc_o[2] * inv, acc_o[3] * inv));
+    else
+      dst[0] = M::round(acc_o[0] * inv);
     if (d == 0 && p.lse)
       p.lse[lse_of(i, hq)] = mx == -INFINITY ? -INFINITY : (mx + log2f(wsum)) * kLn2;
   }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Work lists.

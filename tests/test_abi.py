@@ -116,7 +116,8 @@ def test_plan_fields_are_consistent(lib):
     assert plan.split_keys == 16 * 74  # ceil(1024 granules / 14) = 74
     nrows = 4 * 1 * 32
     o = (14 * nrows * 128 * 4 + 255) // 256 * 256
-    assert plan.workspace_bytes == o + (14 * nrows * 4 + 255) // 256 * 256 + 256  # + counters
+    # + 16 arrival counters, one per 128-byte line
+    assert plan.workspace_bytes == o + (14 * nrows * 4 + 255) // 256 * 256 + 16 * 128
     # the target paged decode workload: packed, one split, no workspace
     code, plan = _plan(lib, batch=32, q_len=1, hq=32, hkv=8, max_L=1100, maxp=69)
     assert (plan.num_splits, plan.pack_gqa, plan.rows_per_block, plan.grid) == (1, 1, 16, 256)
@@ -185,7 +186,7 @@ def test_head_group_plan(lib, kw, per_row):
     nrows = 3 * kw["q_len"] * kw["hq"]
     o = (3 * nrows * d * 4 + 255) // 256 * 256
     assert plan.workspace_bytes == o + (3 * nrows * 4 + 255) // 256 * 256 + (
-        (plan.units * 4 + 255) // 256 * 256)
+        (plan.units * 128 + 255) // 256 * 256)
 
 
 def test_plan_kernel_ids_name_the_tile_and_load_path(lib):
@@ -391,7 +392,7 @@ def test_compact_list_plan(lib, name, kw, want):
     # pairs, which also wait for the sum, halve the arrival counters)
     code0, plan0 = _plan(lib, **dict(kw, sum_L=0, S=plan.num_splits))
     assert plan0.extra_blocks == 0 and plan0.grid == plan0.units * plan0.num_splits
-    counters = lambda p: (p.units * 4 + 255) // 256 * 256 if p.num_splits > 1 else 0
+    counters = lambda p: (p.units * 128 + 255) // 256 * 256 if p.num_splits > 1 else 0
     assert (plan0.workspace_bytes - counters(plan0)) == (plan.workspace_bytes - counters(plan))
     assert plan0.units == plan.units * plan.heads_per_row
     assert plan0.split_keys == plan.split_keys
