@@ -209,6 +209,30 @@ attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const
                             float softmax_scale, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* attn_decode_fwd for callers that cannot allocate or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, layouts, results and errors as
+ * attn_decode_fwd, without workspace / workspace_bytes: a split call keeps
+ * its partials and arrival counters in a scratch array the library holds in
+ * each GPU's memory (16 MiB per GPU, from the first use of the library on
+ * that GPU until the process ends).  The call allocates nothing.
+ *   Limit: a plan (attn_decode_plan with the same shape and options) needs
+ *   the scratch only when num_splits > 1; then it must fit: units * 128
+ *   bytes of counters <= 512 KiB, and the partials (num_splits * rows *
+ *   head_dim * 4 bytes, then num_splits * rows * 4 bytes, each rounded up to
+ *   256 bytes; rows = batch * q_len * num_heads_q) <= 15.5 MiB.  A larger
+ *   call returns ATTN_ERR_WORKSPACE and launches nothing.
+ *   Every call on a GPU shares that GPU's scratch, which keeps the last
+ *   call's partials; calls that overlap on one GPU (other streams or host
+ *   threads) race and must be ordered by the caller.  The kernel leaves the
+ *   counters at zero after every call.
+ *   ATTN_ERR_HIP also when the scratch's device address cannot be found. */
+attn_status attn_decode_fwd_noalloc(const attn_decode_shape* shape, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* cache_seqlens,
+                                    int num_splits, int pack_gqa, float softmax_scale, void* out,
+                                    float* lse, void* stream);
+
 /* Paged decode forward with the options of the flash_attn_with_kvcache call
  * in the lpnh.cn article (section "num_splits 怎么选"): keys appended to the
  * cache in the same call, and a causal mask for q_len > 1 (speculative /

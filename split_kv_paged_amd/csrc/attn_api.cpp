@@ -27,6 +27,7 @@ constexpr int kMaxDevices = 64;
 thread_local attn_plan g_last_plan;
 thread_local bool g_have_last = false;
 std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<void*> g_scratch[kMaxDevices];  // device address of each GPU's scratch array
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -276,9 +277,30 @@ attn_status check_workspace(const attn_plan& plan, void* ws, size_t ws_bytes) {
   return ATTN_OK;
 }
 
+// Where a split call keeps its float32 partials and arrival counters.
+struct WsView {
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
+  int* counters = nullptr;
+};
+
+// The caller's workspace: partial outputs, partial LSEs, then the counters,
+// each at a 256-byte boundary (include/attn_decode.h).
+WsView caller_workspace(const attn_plan& plan, int64_t nrows, int head_dim, void* ws) {
+  WsView v;
+  if (plan.num_splits <= 1) return v;
+  const int64_t o_bytes = round_up(int64_t(plan.num_splits) * nrows * head_dim * 4, 256);
+  const int64_t l_bytes = round_up(int64_t(plan.num_splits) * nrows * 4, 256);
+  v.o_part = static_cast<float*>(ws);
+  v.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+  v.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + o_bytes + l_bytes);
+  return v;
+}
+
 // Launch the split kernel (which merges the splits itself when S > 1).
 attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dtype, int head_dim,
-                void* out, float* lse, void* ws, hipStream_t stream, int64_t max_seqlen_k = 0) {
+                void* out, float* lse, const WsView& ws, hipStream_t stream,
+                int64_t max_seqlen_k = 0) {
   const int S = plan.num_splits;
   prm.num_splits = S;
   prm.split_keys = plan.split_keys;
@@ -295,13 +317,9 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   prm.head_dim = head_dim;
   prm.out = out;
   prm.lse = lse;
-  if (S > 1) {
-    const int64_t o_bytes = round_up(int64_t(S) * prm.nrows * head_dim * 4, 256);
-    const int64_t l_bytes = round_up(int64_t(S) * prm.nrows * 4, 256);
-    prm.o_part = static_cast<float*>(ws);
-    prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
-    prm.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + o_bytes + l_bytes);
-  }
+  prm.o_part = ws.o_part;
+  prm.lse_part = ws.lse_part;
+  prm.counters = ws.counters;
   // Paged calls whose grid needs more than one round run the first split's
   // sequences longest first (ranked inside its workgroups).
   prm.by_length = paged && prm.batch <= skv::kMaxRankBatch && plan.grid > plan.num_cus &&
@@ -314,13 +332,40 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   return ATTN_OK;
 }
 
+// The scratch of attn_decode_fwd_noalloc: counters at its start (a fixed
+// place, so they stay zero from call to call), then the partials.  The
+// device address is looked up once per device, with that device current.
+attn_status scratch_workspace(const attn_plan& plan, int64_t nrows, int head_dim, WsView* v) {
+  *v = WsView{};
+  if (plan.num_splits <= 1) return ATTN_OK;
+  const int64_t c_bytes = int64_t(plan.units) * 4 * skv::kCounterStride;
+  const int64_t o_bytes = round_up(int64_t(plan.num_splits) * nrows * head_dim * 4, 256);
+  const int64_t l_bytes = round_up(int64_t(plan.num_splits) * nrows * 4, 256);
+  if (c_bytes > skv::kScratchCounterBytes ||
+      skv::kScratchCounterBytes + o_bytes + l_bytes > skv::kScratchBytes)
+    return ATTN_ERR_WORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  void* base = g_scratch[dev].load(std::memory_order_acquire);
+  if (!base) {
+    if (skv::scratch_device_address(&base) != hipSuccess || !base) return ATTN_ERR_HIP;
+    g_scratch[dev].store(base, std::memory_order_release);
+  }
+  char* b = static_cast<char*>(base);
+  v->counters = reinterpret_cast<int*>(b);
+  v->o_part = reinterpret_cast<float*>(b + skv::kScratchCounterBytes);
+  v->lse_part = reinterpret_cast<float*>(b + skv::kScratchCounterBytes + o_bytes);
+  return ATTN_OK;
+}
+
 // Paged forward shared by attn_decode_fwd and attn_decode_kvcache_fwd.
 attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k_cache,
                           void* v_cache, const int32_t* block_table, const int32_t* cache_seqlens,
                           const void* k_new, const void* v_new, int new_len, int causal,
                           int num_splits, int pack_gqa, float softmax_scale, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream,
-                          const int32_t* cu_q = nullptr, int total_q = 0) {
+                          const int32_t* cu_q = nullptr, int total_q = 0,
+                          bool use_scratch = false) {
   attn_status st = check_decode_shape(shape);
   if (st != ATTN_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out) return ATTN_ERR_NULL;
@@ -345,7 +390,14 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
                  shape->head_dim, shape->max_seqlen_k, num_splits, pack_gqa, cus, false, &plan,
                  cu_q != nullptr, shape->sum_seqlen_k);
   if (st != ATTN_OK) return st;
-  if ((st = check_workspace(plan, workspace, workspace_bytes)) != ATTN_OK) return st;
+  const int64_t nrows = int64_t(shape->batch) * shape->q_len * shape->num_heads_q;
+  WsView wsv;
+  if (use_scratch) {
+    if ((st = scratch_workspace(plan, nrows, shape->head_dim, &wsv)) != ATTN_OK) return st;
+  } else {
+    if ((st = check_workspace(plan, workspace, workspace_bytes)) != ATTN_OK) return st;
+    wsv = caller_workspace(plan, nrows, shape->head_dim, workspace);
+  }
   if (shape->batch == 0) {
     g_last_plan = plan;
     g_have_last = true;
@@ -391,7 +443,7 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
     a.max_pages = shape->max_pages_per_seq;
     if (skv::launch_append(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
   }
-  return run(plan, p, true, shape->dtype, D, out, lse, workspace, static_cast<hipStream_t>(stream),
+  return run(plan, p, true, shape->dtype, D, out, lse, wsv, static_cast<hipStream_t>(stream),
              shape->max_seqlen_k);
 }
 
@@ -426,6 +478,16 @@ attn_status attn_decode_fwd(const attn_decode_shape* shape, const void* q, const
   return decode_common(shape, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                        block_table, cache_seqlens, nullptr, nullptr, 0, 0, num_splits, pack_gqa,
                        softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_fwd_noalloc(const attn_decode_shape* shape, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* cache_seqlens,
+                                    int num_splits, int pack_gqa, float softmax_scale, void* out,
+                                    float* lse, void* stream) {
+  return decode_common(shape, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                       block_table, cache_seqlens, nullptr, nullptr, 0, 0, num_splits, pack_gqa,
+                       softmax_scale, out, lse, nullptr, 0, stream, nullptr, 0, true);
 }
 
 attn_status attn_decode_varlen_fwd(const attn_decode_shape* shape, const void* q, void* k_cache,
@@ -487,7 +549,9 @@ attn_status attn_dense_fwd(const attn_dense_shape* shape, const void* q, const v
   p.n_sh = shape->q_len;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(D));
   p.scale_log2 = scale * 1.4426950408889634074f;
-  return run(plan, p, false, shape->dtype, D, out, lse, workspace, static_cast<hipStream_t>(stream));
+  return run(plan, p, false, shape->dtype, D, out, lse,
+             caller_workspace(plan, int64_t(shape->num_heads_q) * shape->q_len, D, workspace),
+             static_cast<hipStream_t>(stream));
 }
 
 attn_status attn_combine_fwd(int num_splits, int batch, int q_len, int num_heads, int head_dim,

@@ -71,6 +71,14 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // Arrival counters of the fused combine sit one per 128-byte line: the
 // atomics of different units then never queue on one line.
 constexpr int kCounterStride = 32;  // int32 elements between two units' counters
+// Library-held scratch of attn_decode_fwd_noalloc (scratch.hip): arrival
+// counters first (kScratchCounterBytes, zero between calls: the kernel
+// rearms them), then the float32 partial outputs and LSEs.
+constexpr long kScratchBytes = 16l << 20;
+constexpr long kScratchCounterBytes = 512l << 10;  // 4096 units at kCounterStride
+// Device address of this device's scratch (hipGetSymbolAddress; call with the
+// device current).
+hipError_t scratch_device_address(void** ptr);
 constexpr int kMaxOrderBatch = 1024;  // largest batch of the compact split list (its LDS list)
 // Split-0 workgroups rank the sequences by length (longest first) for
 // batches of at most kMaxRankBatch sequences whose longest has at least
