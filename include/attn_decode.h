@@ -27,8 +27,11 @@
  *   On any error nothing is launched and no output byte is written.
  * - Device-side data (block_table entries, cache_seqlens values) is the
  *   caller's contract: every block_table entry a sequence uses must name a
- *   page < num_pages, and 0 <= cache_seqlens[b] <= max_seqlen_k.  Use
- *   attn_check_paged_inputs() on host copies to verify it in tests.
+ *   page < num_pages, and 0 <= cache_seqlens[b] (+ new_len where keys are
+ *   appended) <= max_seqlen_k.  Use attn_check_paged_inputs() on host
+ *   copies to verify it in tests.  A length over max_seqlen_k gives wrong
+ *   results (keys past the plan's last split are not attended) but leaves
+ *   the workspace's arrival counters intact for later calls.
  * - Element types: q, k, v and out share one 16-bit type (ATTN_FP16 or
  *   ATTN_BF16); lse is float32.  Accumulation is float32 throughout.
  * - An empty sequence (L = 0) gives O = 0 and LSE = -inf.

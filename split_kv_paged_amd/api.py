@@ -3,10 +3,13 @@
 PyTorch provides device memory and the stream; every step of the attention
 runs in the library's HIP kernels.  Functions here check tensor placement,
 dtype and layout, allocate outputs / workspace with torch when the caller
-does not pass them, and call the library on torch's current stream.
+does not pass them, and call the library on torch's current stream, or on
+the stream the caller passes: then the outputs and the zero-filled workspace
+are allocated and filled on that stream too, so the fill is ordered before
+the kernel that relies on it.
 """
+import contextlib
 import ctypes
-import math
 
 import torch
 
@@ -22,6 +25,11 @@ def _ptr(t):
 def _stream(dev, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream):
+    """Allocation context: the caller's stream when one is given."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _need(cond, msg):
@@ -107,7 +115,7 @@ def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pa
     shape = decode_shape(q, k_cache, block_table, max_seqlen_k, sum_seqlen_k)
     lib = _L.load()
     plan = _L.Plan()
-    with torch.cuda.device(dev):
+    with torch.cuda.device(dev), _on(stream):
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         _L.check("attn_decode_plan", lib.attn_decode_plan(ctypes.byref(shape), num_splits,
                                                           pack_gqa, cus, ctypes.byref(plan)))
@@ -180,7 +188,7 @@ def decode_varlen_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlen
               and k_new.dtype == q.dtype and v_new.dtype == q.dtype and k_new.is_contiguous()
               and v_new.is_contiguous(), "k_new / v_new must be contiguous [B, new_len, Hkv, d]")
         new_len = int(k_new.shape[1])
-    with torch.cuda.device(dev):
+    with torch.cuda.device(dev), _on(stream):
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         _L.check("attn_decode_plan", lib.attn_decode_plan(ctypes.byref(shape), num_splits, 1,
                                                           cus, ctypes.byref(plan)))
@@ -216,7 +224,7 @@ def dense_fwd(q, k, v, num_splits=0, softmax_scale=None, out=None, lse=None, ret
     shape = _L.DenseShape(hq, hkv, qlen, kvlen, d, _DT[q.dtype])
     lib = _L.load()
     plan = _L.Plan()
-    with torch.cuda.device(dev):
+    with torch.cuda.device(dev), _on(stream):
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         _L.check("attn_dense_plan", lib.attn_dense_plan(ctypes.byref(shape), num_splits, cus,
                                                         ctypes.byref(plan)))
@@ -242,11 +250,11 @@ def combine_fwd(o_part, lse_part, batch, q_len, num_heads, dtype=torch.bfloat16,
     S, rows, d = o_part.shape
     _need(rows == batch * q_len * num_heads and tuple(lse_part.shape) == (S, rows), "shapes")
     dev = _check_dev(o_part, lse_part, out, lse)
-    if out is None:
-        out = torch.empty((batch, q_len, num_heads, d), dtype=dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((batch, num_heads, q_len), dtype=torch.float32, device=dev)
-    with torch.cuda.device(dev):
+    with torch.cuda.device(dev), _on(stream):
+        if out is None:
+            out = torch.empty((batch, q_len, num_heads, d), dtype=dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((batch, num_heads, q_len), dtype=torch.float32, device=dev)
         code = _L.load().attn_combine_fwd(S, batch, q_len, num_heads, d, _DT[out.dtype],
                                           _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
                                           _stream(dev, stream))
@@ -302,11 +310,12 @@ class PreparedDecode:
         _L.check("attn_decode_plan", self.lib.attn_decode_plan(
             ctypes.byref(self.shape), num_splits, pack_gqa, cus, ctypes.byref(plan)))
         self.plan = plan
-        self.out = out if out is not None else torch.empty_like(q)
-        self.lse = lse if lse is not None else torch.empty(
-            (q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
-        if workspace is None and plan.workspace_bytes > 0:
-            workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        with torch.cuda.device(dev), _on(stream):
+            self.out = out if out is not None else torch.empty_like(q)
+            self.lse = lse if lse is not None else torch.empty(
+                (q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
+            if workspace is None and plan.workspace_bytes > 0:
+                workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         self.workspace = workspace
         self._keep = (q, k_cache, v_cache, block_table, cache_seqlens)
         tail = [int(num_splits), int(pack_gqa), float(softmax_scale) if softmax_scale else 0.0,
@@ -353,11 +362,12 @@ class PreparedDense:
         _L.check("attn_dense_plan", self.lib.attn_dense_plan(
             ctypes.byref(self.shape), num_splits, cus, ctypes.byref(plan)))
         self.plan = plan
-        self.out = out if out is not None else torch.empty_like(q)
-        self.lse = lse if lse is not None else torch.empty((hq, qlen), dtype=torch.float32,
-                                                           device=dev)
-        if workspace is None and plan.workspace_bytes > 0:
-            workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        with torch.cuda.device(dev), _on(stream):
+            self.out = out if out is not None else torch.empty_like(q)
+            self.lse = lse if lse is not None else torch.empty((hq, qlen), dtype=torch.float32,
+                                                               device=dev)
+            if workspace is None and plan.workspace_bytes > 0:
+                workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         self.workspace = workspace
         self._keep = (q, k, v)
         self.args = [ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), int(num_splits),

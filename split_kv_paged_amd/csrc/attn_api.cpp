@@ -300,7 +300,7 @@ WsView caller_workspace(const attn_plan& plan, int64_t nrows, int head_dim, void
 // Launch the split kernel (which merges the splits itself when S > 1).
 attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dtype, int head_dim,
                 void* out, float* lse, const WsView& ws, hipStream_t stream,
-                int64_t max_seqlen_k = 0) {
+                int64_t max_seqlen_k = 0, int64_t sum_seqlen_k = 0) {
   const int S = plan.num_splits;
   prm.num_splits = S;
   prm.split_keys = plan.split_keys;
@@ -321,9 +321,13 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
   prm.lse_part = ws.lse_part;
   prm.counters = ws.counters;
   // Paged calls whose grid needs more than one round run the first split's
-  // sequences longest first (ranked inside its workgroups).
+  // sequences longest first (ranked inside its workgroups).  max_seqlen_k is
+  // only a bound; when the length sum is given, a batch of short sequences
+  // (mean under kMinRankMean keys) is not ranked either, since each
+  // workgroup's round trip for the lengths then outweighs the order.
   prm.by_length = paged && prm.batch <= skv::kMaxRankBatch && plan.grid > plan.num_cus &&
-                  max_seqlen_k >= skv::kMinRankKeys;
+                  max_seqlen_k >= skv::kMinRankKeys &&
+                  (sum_seqlen_k <= 0 || sum_seqlen_k >= int64_t(skv::kMinRankMean) * prm.batch);
   prm.extra_blocks = paged ? plan.extra_blocks : 0;
   if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream) != hipSuccess)
     return ATTN_ERR_HIP;
@@ -444,7 +448,7 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
     if (skv::launch_append(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
   }
   return run(plan, p, true, shape->dtype, D, out, lse, wsv, static_cast<hipStream_t>(stream),
-             shape->max_seqlen_k);
+             shape->max_seqlen_k, shape->sum_seqlen_k);
 }
 
 }  // namespace

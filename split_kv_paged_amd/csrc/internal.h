@@ -92,6 +92,7 @@ constexpr int kMaxOrderBatch = 1024;  // largest batch of the compact split list
 // (1..4096) 189 / 125.
 constexpr int kMaxRankBatch = 256;
 constexpr int kMinRankKeys = 1024;
+constexpr int kMinRankMean = 256;  // with the length sum: mean keys per sequence to rank
 static_assert(kMaxRankBatch % 16 == 0 && kMaxRankBatch <= kMaxOrderBatch, "rank list size");
 
 struct CombineParams {

@@ -280,8 +280,12 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   // Splits of this sequence that hold keys.  Past the last key a split has
   // nothing to add (its LSE would be -inf, weight zero in the combine), so
   // its workgroup leaves at once; a sequence that fits in one split is
-  // finished by split 0 alone, with no partials and no combine.
-  const int nsplit = p.num_splits == 1 ? 1 : max(1, (L + p.split_keys - 1) / p.split_keys);
+  // finished by split 0 alone, with no partials and no combine.  At most
+  // num_splits arrive: a length over max_seqlen_k (outside the contract)
+  // loses its keys past the last split instead of leaving a unit's counter
+  // waiting for a split that never runs.
+  const int nsplit =
+      p.num_splits == 1 ? 1 : min(p.num_splits, max(1, (L + p.split_keys - 1) / p.split_keys));
   if (split >= nsplit) return;
   const bool direct = nsplit == 1;
   const int t1 = min(t0 + p.split_keys, L);

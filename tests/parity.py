@@ -1,13 +1,16 @@
 """Comparison helpers for GPU-vs-oracle parity (no attention arithmetic here).
 
 Tolerances (the bar for every parity test):
-  * outputs in fp16: |gpu - oracle| <= 2e-3 + ulp_fp16(|oracle|)
-  * outputs in bf16: |gpu - oracle| <= 1e-2 + ulp_bf16(|oracle|)
+  * outputs in fp16: |gpu - oracle| <= 2e-3
+  * outputs in bf16: |gpu - oracle| <= 1e-2
   * LSE (float32):  |gpu - oracle| <= 1e-3
   * float32 partial outputs (before the final rounding): <= 1e-3
-The ulp term is the spacing of the output type at the exact value: rounding
-the exact result to fp16/bf16 alone moves it by up to half of that, which
-exceeds the absolute bound wherever |O| >= 8 (fp16) or >= 4 (bf16).
+Rounding the exact result to fp16/bf16 alone moves it by up to half the
+type's spacing at that value, which exceeds the absolute bound wherever
+|O| >= 8 (fp16) or >= 4 (bf16): only such elements (half a spacing above the
+bound, seen with the 8x outlier rows) get one spacing on top of the bound.
+strict=True drops that allowance everywhere (plain max-abs), for workloads
+whose outputs stay below those magnitudes.
 Rows with no keys must be exactly O = 0, LSE = -inf.
 """
 import numpy as np
@@ -43,13 +46,24 @@ def ulp(x, dtype):
     return 2.0 ** (e - 7)
 
 
-def check_out(got_bits, ref, dtype, what="out"):
+def allowance(ref, dtype, strict=False):
+    """Per-element bound: the absolute bar, plus one spacing of the output
+    type where half a spacing exceeds the bar (never with strict)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    allow = np.full(ref.shape, ATOL[dtype])
+    if not strict:
+        sp = ulp(ref, dtype)
+        allow = np.where(0.5 * sp > ATOL[dtype], ATOL[dtype] + sp, allow)
+    return allow
+
+
+def check_out(got_bits, ref, dtype, what="out", strict=False):
     got = W.from_bits(got_bits, dtype).astype(np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), "%s: non-finite output" % what
     err = np.abs(got - ref)
-    allow = ATOL[dtype] + ulp(ref, dtype)
+    allow = allowance(ref, dtype, strict)
     bad = err > allow
     if bad.any():
         idx = np.unravel_index(np.argmax(err - allow), err.shape)
