@@ -51,6 +51,12 @@ extern "C" {
 
 #define ATTN_ABI_VERSION 7
 
+/* Status of every call.  Invalid parameters are refused with an error code
+ * before any work is enqueued, as the MixedQuantSparseFlashMlaMetadata
+ * article's two-phase API does (section 调用方式: ACLNN_ERR_PARAM_INVALID),
+ * and a shape or feature outside the supported envelope is an explicit
+ * error, never a silent fallback to another path (MXFlashAttn page,
+ * sections 前向算子 API and 能力矩阵). */
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
@@ -286,17 +292,26 @@ attn_status attn_decode_varlen_fwd(const attn_decode_shape* shape, const void* q
                                    float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
-/* Plan a dense call (num_splits as above; always packed). */
+/* Plan a dense call (num_splits as above, by the same lpnh.cn rules; always
+ * packed).  The dense problem is the SmallQ README's (section 接口); its
+ * one-core-per-head layout would leave most compute units idle, so the key
+ * range is split as for paged calls (the SmallQ README's 动态 blockK section
+ * sizes the key blocks by the key length). */
 attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,
                             attn_plan* plan);
 
-/* Dense small-query forward (layouts above; other arguments as in
- * attn_decode_fwd; partial rows ordered (hq, i)). */
+/* Dense small-query forward: the SmallQ README's call (section 接口:
+ * query [heads, qLen, headDim] against key/value [heads, kvLen, headDim],
+ * any kvLen and head dim, section 任意 headDim 支持).  Layouts above; other
+ * arguments as in attn_decode_fwd; partial rows ordered (hq, i). */
 attn_status attn_dense_fwd(const attn_dense_shape* shape, const void* q, const void* k,
                            const void* v, int num_splits, float softmax_scale, void* out,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Merge S partials into the final output (the combine step on its own).
+/* Merge S partials into the final output: the combine step on its own, the
+ * reduction of the per-split outputs by their logsumexps that the lpnh.cn
+ * article describes for num_splits > 1 (section 两个开关在 kernel 层面各做了
+ * 什么), written here as the max-shifted log-sum-exp merge.
  *   o_part   float32 [num_splits][rows][head_dim], rows = batch*q_len*num_heads
  *            ordered (b, i, h); lse_part float32 [num_splits][rows]
  *            (natural log; -inf marks an empty partial).
@@ -309,7 +324,10 @@ attn_status attn_combine_fwd(int num_splits, int batch, int q_len, int num_heads
                              int dtype, const float* o_part, const float* lse_part, void* out,
                              float* lse, void* stream);
 
-/* Host check of the device-data contract on host copies of block_table
+/* Host check of the device-data contract of the paged layout (block
+ * table and lengths of the PA_BBND cache, MixedQuantSparseFlashMlaMetadata
+ * article, section 参数说明), with an explicit error code for a bad entry
+ * (section 调用方式), on host copies of block_table
  * [batch, max_pages_per_seq] and cache_seqlens [batch]: every used entry in
  * [0, num_pages) and 0 <= L <= max_seqlen_k.  Returns ATTN_ERR_DATA and the
  * first offending sequence in *bad_batch (may be NULL) on failure. */
@@ -319,13 +337,18 @@ attn_status attn_check_paged_inputs(const attn_decode_shape* shape,
                                     int32_t* bad_batch);
 
 /* Plan recorded by the last successful forward call on this thread
- * (ATTN_ERR_ARG if none yet). */
+ * (ATTN_ERR_ARG if none yet): which kernel ran, with what split count,
+ * packing and grid.  This is the dispatch record the MXFlashAttn page asks
+ * callers to check (section 前向算子 API, get_last_dispatch_info(), and
+ * section 已知限制: assert which kernel actually ran). */
 attn_status attn_last_plan(attn_plan* plan);
 
-/* Static text for a status code. */
+/* Static text for a status code (the explicit errors of the MXFlashAttn
+ * page, section 前向算子 API, readable in logs). */
 const char* attn_status_str(attn_status status);
 
-/* ATTN_ABI_VERSION of the built library. */
+/* ATTN_ABI_VERSION of the built library (this library's own compatibility
+ * check; no page defines it). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus
