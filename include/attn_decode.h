@@ -293,10 +293,10 @@ attn_status attn_decode_varlen_fwd(const attn_decode_shape* shape, const void* q
                                    void* stream);
 
 /* Plan a dense call (num_splits as above, by the same lpnh.cn rules; always
- * packed).  The dense problem is the SmallQ README's (section 接口); its
- * one-core-per-head layout would leave most compute units idle, so the key
- * range is split as for paged calls (the SmallQ README's 动态 blockK section
- * sizes the key blocks by the key length). */
+ * packed).  The dense problem is the SmallQ README's (section 接口), which
+ * walks each head's keys in blocks on one core (section 支持范围); with few
+ * heads that would leave most compute units idle, so the key range is also
+ * split here, as for paged calls (an addition to the README). */
 attn_status attn_dense_plan(const attn_dense_shape* shape, int num_splits, int num_cus,
                             attn_plan* plan);
 
