@@ -309,7 +309,9 @@ def measured_traffic(workload, num_splits):
 
 def cpu_baseline(wl, budget_s):
     """The float64 oracle on the host cores, same workload, a bounded number
-    of repetitions (about budget_s seconds)."""
+    of repetitions (about budget_s seconds).  cores = the worker threads it
+    used: every CPU the process may run on (nproc), at most the oracle's
+    thread cap, one GPU's share of the measurement host."""
     import numpy as np
 
     import oracle
@@ -343,7 +345,8 @@ def cpu_baseline(wl, budget_s):
             "sample": "whole workload (%d query rows, %d keys), %d repetitions, median %.3f s"
                       % (rows, keys, len(times), t),
             "single_thread_value": round(wl.kv_bytes / t1 / 1e9, 4),
-            "host_threads": os.cpu_count()}
+            "nproc": oracle.host_cpus(), "host_threads": os.cpu_count(),
+            "thread_cap": oracle.MAX_THREADS}
 
 
 if __name__ == "__main__":

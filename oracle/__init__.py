@@ -111,9 +111,20 @@ def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+MAX_THREADS = 16  # worker threads at most: one GPU's share of a measurement host's cores
+
+
+def host_cpus():
+    """CPUs this process may run on (the nproc count)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
 def default_threads():
-    """Worker threads: every host core, at most 16."""
-    return max(1, min(16, os.cpu_count() or 1))
+    """Worker threads: every CPU this process may use, at most MAX_THREADS."""
+    return max(1, min(MAX_THREADS, host_cpus()))
 
 
 def decode16(bits, dtype):
