@@ -197,10 +197,19 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   // Q uses it too).
   auto chunk = [](int g_, int kb_) { return kb_ * 4 + g_; };
   // LDS bytes per staged key row: unpadded with the 16-byte chunks of row
-  // r permuted by XOR with f(r) = 2(r & 3) + ((r >> 2) & 1) (needs 8 chunks
-  // a row), else padded by 32 bytes against bank clashes
+  // r permuted by XOR with swz(r) (needs 8 chunks a row), else padded by 32
+  // bytes against bank clashes.  swz(r) = 2(r & 3) + ((r >> 2) & 1), plus 8
+  // ((r >> 2) ^ (r >> 3) & 1) where a row has 16 chunks or more: then the K
+  // reads (16 rows, one chunk each) touch 16 different chunk columns and the
+  // transposed V reads (rows 4g + i, 32-byte pairs of chunks) 8 different
+  // pairs in each half wave, so neither repeats an LDS bank whether a cycle
+  // serves 128 or 256 bytes.  Without the second term rows r and r + 8 (K)
+  // and rows i and 4 + i (V) shared banks at 256 bytes a cycle.
   constexpr bool kSwz = D >= 64;
   constexpr int ROWB = kSwz ? D * 2 : D * 2 + 32;
+  auto swz = [](int r) {
+    return 2 * (r & 3) + ((r >> 2) & 1) + (D >= 128 ? 8 * (((r >> 2) ^ (r >> 3)) & 1) : 0);
+  };
   // NBUF == 0: no register ring; each tile goes from memory straight into
   // the wave's LDS slot, one tile in flight per wave while the previous one
   // is computed
@@ -317,8 +326,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
         const long n = row_of(rowq / p.heads_per_unit, hq0 + rowq % p.heads_per_unit);
         v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd)[cc];
       }
-      const int f = 2 * (rr & 3) + ((rr >> 2) & 1);
-      *reinterpret_cast<uint4*>(s_q + rr * (D * 2) + ((cc ^ f) * 16)) = v;
+      *reinterpret_cast<uint4*>(s_q + rr * (D * 2) + ((cc ^ swz(rr & 15)) * 16)) = v;
     }
     __syncthreads();
   }
@@ -352,13 +360,14 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   uint8_t* const my_k = my_v + kTile * ROWB;  // (direct-to-LDS tiles only)
   typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
   const uint32_t v_wr = uint32_t(n16 * ROWB);  // row of this lane's V bytes (unswizzled)
-  const int f_wr = 2 * (n16 & 3) + ((n16 >> 2) & 1);            // chunk XOR of row n16
+  const int f_wr = swz(n16);  // chunk XOR of row n16
   // transposed read of d block db: lane 16g + 4i + q reads key 4g+i, d 16db + 4q .. +3
   const uint32_t v_rd = uint32_t((4 * g + ((lane & 15) >> 2)) * ROWB + (lane & 3) * 8);
-  // swizzled: row 4g+i, chunk 2db + (q>>1) lands at chunk 2(db^i) + ((q>>1)^(g&1))
+  // swizzled: row r = 4g+i, chunk 2db + (q>>1) lands at chunk
+  // 2(db ^ (swz(r) >> 1)) + ((q>>1) ^ (swz(r) & 1)), with swz(r) & 1 = g & 1
   const uint32_t v_rd_swz = uint32_t((4 * g + ((lane & 15) >> 2)) * ROWB +
                                      (((lane & 3) >> 1) ^ (g & 1)) * 16 + (lane & 1) * 8);
-  const int i_rd = (lane & 15) >> 2;
+  const int i_rd = swz(4 * g + ((lane & 15) >> 2)) >> 1;
 
   auto tile_row0 = [&](int idx, int page) -> long {
     const int tt = t0 + (wave + idx * NW) * kTile;
@@ -545,7 +554,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int row = j * kRPI + lane / kCPR;
-      const int ch = (lane % kCPR) ^ (2 * (row & 3) + ((row >> 2) & 1));
+      const int ch = (lane % kCPR) ^ swz(row);
       const int off = (GEN == 0 || ch * 8 < kvd) ? int(row * row_stride * 2) + ch * 16 : kPastEnd;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(my_k + j * 1024), 16, off, 0, 0, kStream);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(my_v + j * 1024), 16, off, 0, 0, kStream);
