@@ -785,6 +785,56 @@ def test_bitwise_determinism_and_page_permutation():
         assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+def test_fused_combine_soak():
+    """Bounded soak of the fused combine (partials written through, the
+    arrival atomic, the last split's merge): 240 seeded split calls over 12
+    ragged shapes, each call repeated on a workspace shared by every call of
+    its shape, and with the compact list, and compared bit for bit with a
+    first split-major run.  A stale partial or a counter not rearmed would
+    change some output; the test stops at the first mismatch."""
+    rng = np.random.default_rng(4242)
+    shapes = []
+    for k in range(12):
+        dt = ("bf16", "fp16")[k % 2]
+        d = (128, 64, 128, 256)[k % 4]
+        hkv = (8, 4, 2, 8)[k % 4]
+        G = (4, 2, 8, 1)[k % 4]
+        B = int(rng.integers(2, 24))
+        lens = [int(x) for x in rng.integers(0, 6000, B)]
+        lens[0] = 6000
+        S = int(rng.integers(2, 17))
+        shapes.append((dt, B, hkv * G, hkv, d, lens, S))
+    calls = 0
+    for k, (dt, B, hq, hkv, d, lens, S) in enumerate(shapes):
+        wl = W.make_paged(4300 + k, dt, B, 1, hq, hkv, d, 16, lens, spare_pages=1)
+        q, kc, vc = to_dev(wl.q, dt), to_dev(wl.k_cache, dt), to_dev(wl.v_cache, dt)
+        bt, sl = i32_dev(wl.block_table), i32_dev(wl.cache_seqlens)
+        case("soak %d: %s B%d Hq%d/Hkv%d d%d S=%d, 20 calls" % (k, dt, B, hq, hkv, d, S))
+        ref, ref_l = None, None
+        ws = {}
+        for rep in range(20):
+            hint = int(sum(lens)) if rep % 2 else None
+            key = hint is not None
+            out, lse = api.decode_fwd(q, kc, vc, bt, sl, num_splits=S, softmax_scale=wl.scale,
+                                      max_seqlen_k=wl.max_seqlen_k, sum_seqlen_k=hint,
+                                      workspace=ws.get(key))
+            if key not in ws:
+                plan = api.last_plan()
+                ws[key] = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()
+            o, l = bits_of(out), lse.cpu().numpy()
+            if ref is None:
+                ref, ref_l = o, l
+                ro, rl = oracle_paged(wl)
+                check_out(o, ro, dt, "soak %d" % k)
+                check_lse(l, rl)
+            else:
+                assert np.array_equal(o, ref), "soak %d call %d: output differs" % (k, rep)
+                assert np.array_equal(l.view(np.uint32), ref_l.view(np.uint32)), (k, rep)
+            calls += 1
+    print("  %d split calls, all bitwise equal to the first run of their shape" % calls, flush=True)
+
+
 @pytest.mark.parametrize("length_sum,d", [(False, 128), (True, 128), (True, 64)],
                          ids=["split-major", "compact", "compact-head-pairs"])
 def test_hip_graph_replays_match_eager(length_sum, d):
