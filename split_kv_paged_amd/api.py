@@ -100,7 +100,9 @@ def decode_fwd(q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0, pa
     block_table int32 [B, max_pages]; cache_seqlens int32 [B].
     Returns (out [B, q_len, Hq, d], lse float32 [B, Hq, q_len] or None).
     max_seqlen_k (a host int bound on the attended lengths) drives the plan;
-    by default it is max_pages * page_size, which needs no device sync.
+    by default it is max_pages * page_size, which needs no device sync.  A
+    tight bound matters for speed: the split count, the split length and
+    the longest-first ordering are all chosen from it.
     k_new / v_new [B, new_len, Hkv, d]: keys written into the cache at
     positions cache_seqlens[b].. before attention (attn_decode_kvcache_fwd);
     causal: query i of q_len sees keys j <= L - q_len + i.

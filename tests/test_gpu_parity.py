@@ -835,6 +835,45 @@ def test_fused_combine_soak():
     print("  %d split calls, all bitwise equal to the first run of their shape" % calls, flush=True)
 
 
+@pytest.mark.parametrize("q_len,G,d,length_sum", [(1, 4, 128, False), (1, 2, 64, True),
+                                                  (4, 8, 128, False), (8, 8, 128, True),
+                                                  (8, 4, 64, False), (2, 4, 256, False)],
+                         ids=["rows4", "pairs-compact", "rows32", "rows64-compact", "rows32-d64",
+                              "d256"])
+def test_split_calls_repeat_on_one_workspace(q_len, G, d, length_sum):
+    """Split calls with one, two and four 16-row blocks per workgroup, with
+    and without the compact list, twice on one workspace: the arrival
+    counters are zero after each call, the second output is the first bit
+    for bit, and both are within the bar of the oracle."""
+    hkv = 2
+    lens = [900, 5, 2100, 1300, 0]
+    wl = W.make_paged(5100 + q_len * 10 + d, "bf16", len(lens), q_len, hkv * G, hkv, d, 16, lens,
+                      spare_pages=1)
+    q, kc, vc = to_dev(wl.q, "bf16"), to_dev(wl.k_cache, "bf16"), to_dev(wl.v_cache, "bf16")
+    bt, sl = i32_dev(wl.block_table), i32_dev(wl.cache_seqlens)
+    hint = int(sum(lens)) if length_sum else None
+    case("split calls on one workspace: q_len %d G %d d %d, length sum %s"
+         % (q_len, G, d, length_sum))
+    plan = api.decode_plan(len(lens), q_len, hkv * G, hkv, d, 16, wl.block_table.shape[1],
+                           wl.max_seqlen_k, torch.bfloat16, num_splits=3, sum_seqlen_k=hint or 0)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    nrows = len(lens) * q_len * hkv * G
+    c0 = (3 * nrows * d * 4 + 255) // 256 * 256 + (3 * nrows * 4 + 255) // 256 * 256
+    res = []
+    for _ in range(2):
+        out, lse = api.decode_fwd(q, kc, vc, bt, sl, num_splits=3, softmax_scale=wl.scale,
+                                  max_seqlen_k=wl.max_seqlen_k, sum_seqlen_k=hint, workspace=ws)
+        torch.cuda.synchronize()
+        assert int((ws[c0:] != 0).sum()) == 0, "arrival counters not rearmed"
+        res.append((bits_of(out), lse.cpu().numpy()))
+    assert api.last_plan().num_splits == 3
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1].view(np.uint32), res[1][1].view(np.uint32))
+    ro, rl = oracle_paged(wl)
+    check_out(res[0][0], ro, "bf16", "split calls on one workspace")
+    check_lse(res[0][1], rl)
+
+
 @pytest.mark.parametrize("length_sum,d", [(False, 128), (True, 128), (True, 64)],
                          ids=["split-major", "compact", "compact-head-pairs"])
 def test_hip_graph_replays_match_eager(length_sum, d):
