@@ -6,6 +6,17 @@
 
 namespace skv {
 
+// Division of a non-negative 32-bit integer by a divisor fixed for the
+// launch, as a multiply-high, a subtract and two shifts (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994:
+// the round-up method, exact for every 32-bit dividend):
+//   l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+//   t = (n * m) >> 32, n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0).
+struct FastDiv {
+  uint32_t m;
+  int s1, s2;
+};
+
 // One split-kernel launch.  Rows: a "row" is one (b, i, hq) query vector.
 //   first query of sequence b: qb = cu_q ? cu_q[b] : b * q_len
 //   row index n(b, i, hq) = (qb + i) * n_si + hq * n_sh
@@ -52,6 +63,11 @@ struct SplitParams {
   int causal;          // query i of q_len sees keys j <= L - q_len + i
   const int32_t* cu_q; // varlen: queries of sequence b are rows cu_q[b] .. cu_q[b+1]-1
   int total_q;         // varlen: cu_q[batch]; lse is [Hq, total_q]
+  // Filled by launch_split_mfma from the fields above: division by
+  // batch * unit_heads * row_blocks, unit_heads, group, heads_per_unit,
+  // page_size, split_keys and (head groups) the query heads per KV head,
+  // heads_per_unit * head_dim / 128.
+  FastDiv fd_units, fd_unit_heads, fd_group, fd_hpu, fd_page, fd_split_keys, fd_gq;
 };
 
 // Append new_len keys per sequence to the paged cache (before attention):

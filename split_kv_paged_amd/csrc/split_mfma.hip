@@ -130,6 +130,13 @@ constexpr int kPastEnd = 0x7FFFFFF0;  // beyond any tile's range (tiles are < 2 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// n / d for n >= 0 (d's FastDiv); the same code on scalar or vector values
+__device__ __forceinline__ int fdiv(int n, FastDiv d) {
+  const uint32_t u = uint32_t(n);
+  const uint32_t t = __umulhi(u, d.m);
+  return int((t + ((u - t) >> d.s1)) >> d.s2);
+}
+
 // Partials shared between workgroups on different XCDs go straight to and
 // from memory: stores and loads carry the sc0|sc1 (system coherence) cache
 // policy, so they are written through and read past every cache, and no
@@ -239,7 +246,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   // first tile column of packed row pr's head (head groups: slice
   // (pr mod R*G) / G of the row, G = heads_per_unit * head_dim / D)
   auto col0 = [&](int pr) {
-    return kGroup ? ((pr % p.heads_per_unit) / (p.heads_per_unit * hd / D)) * hd : 0;
+    return kGroup ? fdiv(pr - fdiv(pr, p.fd_hpu) * p.heads_per_unit, p.fd_gq) * hd : 0;
   };
 
   struct Buf {
@@ -253,14 +260,14 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   const int g = lane >> 4;    // S^T: key group (keys 4g..4g+3); O: rows 4g..4g+3
 
   const int hq0 = uh * p.heads_per_unit;
-  const int h = hq0 / p.group;
+  const int h = p.heads_per_unit == p.group ? uh : fdiv(hq0, p.fd_group);
 
   // split range and this wave's tiles (round-robin over the waves)
   const int t0 = split * p.split_keys;
   auto load_pages = [&](int cb) -> int {
     if constexpr (PAGED) {
       const int tt = t0 + (wave + (cb + lane) * NW) * kTile;
-      return p.block_table[(long)b * p.max_pages + min(tt / p.page_size, p.max_pages - 1)];
+      return p.block_table[(long)b * p.max_pages + min(fdiv(tt, p.fd_page), p.max_pages - 1)];
     } else {
       return 0;
     }
@@ -304,7 +311,8 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   // loses its keys past the last split instead of leaving a unit's counter
   // waiting for a split that never runs.
   const int nsplit =
-      p.num_splits == 1 ? 1 : min(p.num_splits, max(1, (L + p.split_keys - 1) / p.split_keys));
+      p.num_splits == 1 ? 1
+                        : min(p.num_splits, max(1, fdiv(L + p.split_keys - 1, p.fd_split_keys)));
   if (split >= nsplit) return;
   const bool direct = nsplit == 1;
   const int t1 = min(t0 + p.split_keys, L);
@@ -321,7 +329,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   if (p.causal) {
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-      const int i_row = (row0 + 16 * r + n16) / p.heads_per_unit;
+      const int i_row = fdiv(row0 + 16 * r + n16, p.fd_hpu);
       lim[r] = min(t1, max(0, L - qlen_b + 1 + i_row));
     }
   }
@@ -333,7 +341,8 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       const int rowq = row0 + rr;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (rowq < rows_b) {
-        const long n = row_of(rowq / p.heads_per_unit, hq0 + rowq % p.heads_per_unit);
+        const int iq = fdiv(rowq, p.fd_hpu);
+        const long n = row_of(iq, hq0 + rowq - iq * p.heads_per_unit);
         v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + n * hd)[cc];
       }
       *reinterpret_cast<uint4*>(s_q + rr * (D * 2) + ((cc ^ swz(rr & 15)) * 16)) = v;
@@ -383,7 +392,8 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   auto tile_row0 = [&](int idx, int page) -> long {
     const int tt = t0 + (wave + idx * NW) * kTile;
     if constexpr (PAGED) {
-      return ((long)page * p.page_size + tt % p.page_size) * p.hkv * kvd + (long)h * kvd;
+      return ((long)page * p.page_size + tt - fdiv(tt, p.fd_page) * p.page_size) * p.hkv * kvd +
+             (long)h * kvd;
     } else {
       return ((long)h * p.kv_len + tt) * kvd;
     }
@@ -431,8 +441,8 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       const bool real = rowq < rows_b;
       long n = 0;
       if (real) {
-        const int i = rowq / p.heads_per_unit;
-        const int hq = hq0 + rowq % p.heads_per_unit;
+        const int i = fdiv(rowq, p.fd_hpu);
+        const int hq = hq0 + rowq - i * p.heads_per_unit;
         n = row_of(i, hq);
       }
       if constexpr (GEN == 2) {
@@ -710,8 +720,8 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
           o[0] = fmaf(wt, a[0], o[0]);
         }
       }
-      const int i = pr / p.heads_per_unit;
-      const int hq = hq0 + pr % p.heads_per_unit;
+      const int i = fdiv(pr, p.fd_hpu);
+      const int hq = hq0 + pr - i * p.heads_per_unit;
       const long nrow = row_of(i, hq);
       if (direct) {
         uint16_t* dst = static_cast<uint16_t*>(p.out) + nrow * hd + d;
@@ -763,8 +773,8 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
     const int r = t / hd;
     const int d = t % hd;
     const int pr = row0 + r;
-    const int i = pr / p.heads_per_unit;
-    const int hq = hq0 + pr % p.heads_per_unit;
+    const int i = fdiv(pr, p.fd_hpu);
+    const int hq = hq0 + pr - i * p.heads_per_unit;
     const long nrow = row_of(i, hq);
     float mx = -INFINITY, wsum = 0.f;  // log2 units
     float acc_o[VEC];
@@ -861,7 +871,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     const int per_seq = p.unit_heads * p.row_blocks;
     for (int i = threadIdx.x; i < p.batch; i += NW * 64) {
       const int L = p.seqlens[i] + p.seq_add;
-      const int more = L > p.split_keys ? (L - 1) / p.split_keys : 0;
+      const int more = L > p.split_keys ? fdiv(L - 1, p.fd_split_keys) : 0;
       s_seq[i + 1] = min(more, p.num_splits - 1) * per_seq;
     }
     if (threadIdx.x == 0) s_seq[0] = 0;
@@ -895,12 +905,12 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       // every lane found the same values: keep them scalar
       const int bs = __builtin_amdgcn_readfirstlane(lo);
       const int r = __builtin_amdgcn_readfirstlane(item - s_seq[lo]);
-      const int rem = r % per_seq;
       // The thread index passes through an empty asm, so that nothing the
       // unit derives from it is hoisted out of this loop and kept live
       // across it (that raised the kernel's VGPR count by a third).
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
+      const int rem = r % per_seq;
       split_unit<DT, D, NW, NBUF, PAGED, GEN, NRB>(p, 1 + r / per_seq, bs, rem % p.unit_heads,
                                                   rem / p.unit_heads, tid);
       __syncthreads();  // the unit's LDS is reused by the next one
@@ -909,16 +919,17 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
   }
   const int units = p.batch * p.unit_heads * p.row_blocks;
   const int id0 = int(blockIdx.x) - (EXTRA ? p.extra_blocks : 0);
-  const int split = EXTRA ? 0 : p.num_splits - 1 - id0 / units;
+  const int sq = EXTRA ? 0 : fdiv(id0, p.fd_units);
+  const int split = EXTRA ? 0 : p.num_splits - 1 - sq;
   int rb, bid;
   {
     const int pairs = p.batch * p.unit_heads;
-    const int id = id0 % units;
-    const int grp = id / (8 * p.row_blocks);
+    const int id = id0 - sq * units;
+    const int grp = p.row_blocks == 1 ? id >> 3 : id / (8 * p.row_blocks);
     const int rem = id - grp * 8 * p.row_blocks;
     const int n = min(8, pairs - grp * 8);
-    rb = rem / n;
-    int j = rem % n;
+    rb = n == 8 ? rem >> 3 : rem / n;
+    int j = rem - rb * n;
     if constexpr (PAGED && (GEN == 0 || GEN == 3) && (D == 128 || D == 64)) {
       // A unit's slice of a key row is D * 2 bytes (256 or 128) at offset
       // h * D * 2, h the unit's KV head (head group).  Packed, with a
@@ -933,8 +944,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     }
     bid = grp * 8 + j;
   }
-  const int uh = bid % p.unit_heads;
-  int b = bid / p.unit_heads;
+  int b = fdiv(bid, p.fd_unit_heads);
+  const int uh = bid - b * p.unit_heads;
   if (PAGED && p.by_length && split == 0) {
     // Rank of sequence i: the sequences longer than it, plus the equally
     // long ones before it.  Four adjacent threads share a sequence, each
@@ -1040,8 +1051,27 @@ hipError_t launch_mfma_dt(const SplitParams& p, int grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_split_mfma(int dtype, bool paged, const SplitParams& p, int grid, hipStream_t s) {
+FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  const int l = d <= 1 ? 0 : 32 - __builtin_clz(d - 1);  // ceil(log2 d)
+  f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 1 ? l - 1 : 0;
+  return f;
+}
+
+hipError_t launch_split_mfma(int dtype, bool paged, const SplitParams& prm, int grid,
+                             hipStream_t s) {
   if (grid <= 0) return hipSuccess;
+  SplitParams p = prm;
+  auto pos = [](long v) { return uint32_t(v > 1 ? v : 1); };
+  p.fd_units = make_fastdiv(pos((long)p.batch * p.unit_heads * p.row_blocks));
+  p.fd_unit_heads = make_fastdiv(pos(p.unit_heads));
+  p.fd_group = make_fastdiv(pos(p.group));
+  p.fd_hpu = make_fastdiv(pos(p.heads_per_unit));
+  p.fd_page = make_fastdiv(pos(p.page_size));
+  p.fd_split_keys = make_fastdiv(pos(p.split_keys));
+  p.fd_gq = make_fastdiv(pos(p.head_group > 1 ? (long)p.heads_per_unit * p.head_dim / 128 : 1));
   if (paged)
     return dtype == 1 ? launch_mfma_dt<1, true>(p, grid, s) : launch_mfma_dt<0, true>(p, grid, s);
   return dtype == 1 ? launch_mfma_dt<1, false>(p, grid, s) : launch_mfma_dt<0, false>(p, grid, s);
