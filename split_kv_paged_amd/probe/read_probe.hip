@@ -82,6 +82,9 @@ __device__ __forceinline__ u32x4_t ld_buf(__amdgpu_buffer_rsrc_t r, int off) {
 // One workgroup of 16 waves per (split s, sequence b, KV head h), split-major
 // like the decode kernel's grid; wave w takes the 16-key tiles w, w + 16, ...
 // of the split's keys [s C, min((s + 1) C, L_b)) with one tile in flight.
+// The decode kernel's XCD order too: in each full group of 8 (b, h) units,
+// XCDs 0-3 (workgroup index mod 8) read the slices whose byte offset in the
+// key row has bit 8 clear, XCDs 4-7 the others.
 // CPR: 16-byte chunks per key row (head_dim / 8).  Chunk j = lane + 64 u of
 // a tile is row j / CPR, column chunk j % CPR, so one load instruction
 // covers 64 / CPR whole rows.  A tile's descriptors end after its last
@@ -92,8 +95,17 @@ __global__ __launch_bounds__(kPageWaves * 64) void page_read_kernel(const PagePr
   static_assert(kPer >= 1, "head_dim >= 32");
   const int units = p.batch * p.hkv;
   const int split = int(blockIdx.x) / units;
-  const int b = (int(blockIdx.x) % units) / p.hkv;
-  const int h = int(blockIdx.x) % p.hkv;
+  int u = int(blockIdx.x) % units;
+  constexpr int kSlice = CPR * 16;  // bytes of one head's slice of a key row
+  if constexpr (kSlice == 256 || kSlice == 128) {
+    constexpr int kSlices = 512 / kSlice;
+    if (p.hkv % kSlices == 0 && (u | 7) < units) {
+      const int x = int(blockIdx.x) & 7, k = x & 3, half = x >> 2;
+      u = (u & ~7) | (kSlice == 256 ? 2 * k + half : (k & 1) + 4 * (k >> 1) + 2 * half);
+    }
+  }
+  const int b = u / p.hkv;
+  const int h = u % p.hkv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = split * p.split_keys;
@@ -134,7 +146,7 @@ __global__ __launch_bounds__(kPageWaves * 64) void page_read_kernel(const PagePr
     }
   }
   const uint32_t t = block_sum(s);
-  if (threadIdx.x == 0) p.sums[blockIdx.x] = t;
+  if (threadIdx.x == 0) p.sums[(long)split * units + u] = t;  // [s, b, h]
 }
 
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
