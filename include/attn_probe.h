@@ -44,9 +44,9 @@ attn_status attn_probe_stream_read(const void* a, size_t a_bytes, const void* b,
  * flight: per tile the 16 K rows and the 16 V rows of head h, with 16-byte
  * non-temporal loads.  Physical pages come from block_table, 64 tiles per
  * load.  Units go to XCDs as in the decode kernel (in each group of 8
- * consecutive (b, h), XCDs 0-3 read the slices whose offset in the key row
- * has bit 8 clear).  (Sixteen waves with one tile each read as fast as the
- * best of the deeper per-wave pipelines tried with 8 waves.)
+ * consecutive (b, h), XCD x reads the slice whose offset in the key row has
+ * bit 9 equal to bit 0 of x).  (Sixteen waves with one tile each read as
+ * fast as the best of the deeper per-wave pipelines tried with 8 waves.)
  *   shape        as for attn_decode_fwd (q_len, num_heads_q, dtype and
  *                sum_seqlen_k are not used); head_dim 32, 64, 128 or 256
  *   k_cache,

@@ -849,14 +849,13 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 // that XCD's L2.  Head units go in groups of 8: workgroup g*8*row_blocks +
 // rb*n + i runs a head unit 8g + j, row block rb, where n = 8 except in the
 // last, shorter group.  Within a full group the unit follows the XCD
-// (paged calls): a unit's KV slice of each key row starts at a byte offset
-// whose bit 8 is 0 or 1 (head_dim 128: even or odd KV head), and when a
-// group holds four of each, XCDs 0-3 read the bit-0 slices and XCDs 4-7
-// the bit-1 slices.  Measured on the paged GQA-4 d 128 workload (KV head h
-// of every sequence on XCD h before, so even and odd slices met on every
-// half): 24.8 -> 23.7 us; per XCD, odd heads' loops had run 15-18%
-// longer than even heads', and the launch ended with them.  Otherwise
-// j = i.
+// (paged calls): XCD x reads the units whose slice of each key row starts
+// at a byte offset with bit 9 equal to bit 0 of x and, where the slice
+// offsets reach it, bit 10 equal to bit 1 of x.  Found by sweeping head ->
+// XCD permutations (MI355X, paged GQA-4 bf16 d 128, us): identity (KV
+// head h on XCD h) 24.7, the kept map 23.7, the other maps tried 24.1 to
+// 24.9; 64 sequences of 2048 keys 87.3 -> 84.0; fp16 d 64 (128-byte
+// slices, no head pairs) 51.7 -> 51.2.  Otherwise j = i.
 // EXTRA: a kernel built for the compact list (its loop over items costs
 // about ten VGPRs, so the split-major kernels are built without it).
 template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB, bool EXTRA>
@@ -933,13 +932,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     if constexpr (PAGED && (GEN == 0 || GEN == 3) && (D == 128 || D == 64)) {
       // A unit's slice of a key row is D * 2 bytes (256 or 128) at offset
       // h * D * 2, h the unit's KV head (head group).  Packed, with a
-      // multiple of kPer units per sequence, member m of a full group of 8
-      // has bit 8 of that offset equal to bit 0 (D 128) or bit 1 (D 64) of
-      // m, and the key rows start at multiples of 512 bytes.
-      constexpr int kPer = 512 / (D * 2);
+      // multiple of kPer units per sequence (key rows of at least 1 KiB),
+      // member m of a full group of 8 has its slice at offset bits 8-10
+      // (D 128) or 7-9 (D 64) equal to the bits of m.  XCD x takes the
+      // member whose offset bit 9 is bit 0 of x, and (D 128) bit 10 bit 1.
+      constexpr int kPer = 1024 / (D * 2);
       if (n == 8 && p.heads_per_unit == p.group && p.unit_heads % kPer == 0) {
-        const int x = int(blockIdx.x) & 7, k = x & 3, half = x >> 2;
-        j = D == 128 ? 2 * k + half : (k & 1) + 4 * (k >> 1) + 2 * half;
+        const int x = int(blockIdx.x) & 7;
+        j = D == 128 ? 2 * (x & 3) + (x >> 2) : 4 * (x & 1) + (x >> 1);
       }
     }
     bid = grp * 8 + j;

@@ -83,8 +83,9 @@ __device__ __forceinline__ u32x4_t ld_buf(__amdgpu_buffer_rsrc_t r, int off) {
 // like the decode kernel's grid; wave w takes the 16-key tiles w, w + 16, ...
 // of the split's keys [s C, min((s + 1) C, L_b)) with one tile in flight.
 // The decode kernel's XCD order too: in each full group of 8 (b, h) units,
-// XCDs 0-3 (workgroup index mod 8) read the slices whose byte offset in the
-// key row has bit 8 clear, XCDs 4-7 the others.
+// XCD x (workgroup index mod 8) reads the slice whose byte offset in the
+// key row has bit 9 equal to bit 0 of x (and, 256-byte slices, bit 10 equal
+// to bit 1 of x).
 // CPR: 16-byte chunks per key row (head_dim / 8).  Chunk j = lane + 64 u of
 // a tile is row j / CPR, column chunk j % CPR, so one load instruction
 // covers 64 / CPR whole rows.  A tile's descriptors end after its last
@@ -98,10 +99,10 @@ __global__ __launch_bounds__(kPageWaves * 64) void page_read_kernel(const PagePr
   int u = int(blockIdx.x) % units;
   constexpr int kSlice = CPR * 16;  // bytes of one head's slice of a key row
   if constexpr (kSlice == 256 || kSlice == 128) {
-    constexpr int kSlices = 512 / kSlice;
+    constexpr int kSlices = 1024 / kSlice;
     if (p.hkv % kSlices == 0 && (u | 7) < units) {
-      const int x = int(blockIdx.x) & 7, k = x & 3, half = x >> 2;
-      u = (u & ~7) | (kSlice == 256 ? 2 * k + half : (k & 1) + 4 * (k >> 1) + 2 * half);
+      const int x = int(blockIdx.x) & 7;
+      u = (u & ~7) | (kSlice == 256 ? 2 * (x & 3) + (x >> 2) : 4 * (x & 1) + (x >> 1));
     }
   }
   const int b = u / p.hkv;

@@ -874,6 +874,29 @@ def test_split_calls_repeat_on_one_workspace(q_len, G, d, length_sum):
     check_lse(res[0][1], rl)
 
 
+@pytest.mark.parametrize("dt,B,hkv,G,d,length_sum,pack", [
+    ("bf16", 3, 8, 4, 128, False, -1),   # full groups of one sequence's 8 KV heads
+    ("bf16", 5, 4, 8, 128, False, -1),   # groups spanning two sequences, a short last group
+    ("fp16", 4, 8, 2, 64, False, -1),    # 128-byte slices
+    ("fp16", 3, 16, 1, 64, False, -1),   # G = 1, 16 KV heads
+    ("fp16", 6, 8, 2, 64, True, -1),     # head pairs (256-byte group slices), compact list
+    ("bf16", 3, 8, 4, 128, False, 0),    # unpacked: units are query heads, no reordering
+], ids=["d128-h8", "d128-h4", "d64-h8", "d64-h16-mha", "pairs", "unpacked"])
+def test_xcd_order_of_units(dt, B, hkv, G, d, length_sum, pack):
+    """Head units reordered by XCD within groups of 8 workgroups: every unit
+    is computed exactly once (each output row against the oracle), with
+    and without splits."""
+    lens = [int(x) for x in np.random.default_rng(B * 100 + d + hkv).integers(1, 2500, B)]
+    wl = W.make_paged(6100 + B + d + hkv, dt, B, 1, hkv * G, hkv, d, 16, lens, spare_pages=1)
+    ro, rl = oracle_paged(wl)
+    for S in (1, 3):
+        case("XCD order: %s B%d Hkv%d G%d d%d sum %s pack %d S=%d" % (dt, B, hkv, G, d, length_sum,
+                                                                   pack, S))
+        out, lse, plan = run_paged(wl, num_splits=S, pack_gqa=pack, sum_hint=length_sum)
+        check_out(out, ro, dt, "XCD order", strict=True)
+        check_lse(lse, rl)
+
+
 @pytest.mark.parametrize("length_sum,d", [(False, 128), (True, 128), (True, 64)],
                          ids=["split-major", "compact", "compact-head-pairs"])
 def test_hip_graph_replays_match_eager(length_sum, d):

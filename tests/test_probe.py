@@ -117,7 +117,7 @@ PAGE_CASES = [
     (64, "fp16", 4, 1, 32, 48, [95, 96, 97, 1], 0),
     (65, "bf16", 4, 2, 128, 16, [1000, 0, 257, 16], 256),  # splits, some empty
     (66, "fp16", 2, 3, 64, 32, [5000, 4000], 2048),
-    (67, "fp16", 4, 4, 64, 16, [700, 33, 1200, 5], 0),  # XCD order of 128-byte slices
+    (67, "fp16", 4, 8, 64, 16, [700, 33, 1200, 5], 0),  # XCD order of 128-byte slices
 ]
 
 
