@@ -20,7 +20,9 @@
  * ---------------------------------------
  * - Pointers to tensors are DEVICE pointers owned by the caller.  The
  *   library never allocates, frees or keeps them; it keeps no state between
- *   calls except the thread-local record read by attn_last_plan().
+ *   calls except the thread-local record read by attn_last_plan() and the
+ *   per-GPU scratch array of attn_decode_fwd_noalloc() (with its device
+ *   address, looked up once per GPU).
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Work is enqueued on it and the call returns without waiting.
  * - All arguments are validated on the host before anything is enqueued.
