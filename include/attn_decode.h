@@ -105,7 +105,10 @@ typedef struct {
                             * the mean length) whose longest sequence exceeds
                             * two compute units' fair shares of all keys,
                             * into pieces of at most two thirds of a share (an
-                            * addition to the pages' rule), and a split call
+                            * addition to the pages' rule), raises a split
+                            * count above 1 that leaves compute units idle
+                            * until the workgroups fill them (another
+                            * addition), and a split call
                             * may launch the compact list (see
                             * attn_plan.extra_blocks) instead of every
                             * (unit, split) pair, and a head-dim-64 or -32

@@ -335,7 +335,8 @@ RAGGED_CASES = [
     # near-uniform lengths: share = 8 * 32002 / 256 = 1000.06; 1100 <= 2000: rule's 1
     ("uniform ~1000", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=69, max_L=1100, sum_L=32002), 1),
     # long uniform context, GQA-8: max_L = mean, not ragged: the rule's 14
-    ("long uniform", dict(batch=4, q_len=1, hq=32, hkv=4, maxp=1024, max_L=16384, sum_L=65536), 14),
+    # leaves 256 - 16 * 14 = 32 CUs idle; with the sum, 256 / 16 = 16
+    ("long uniform", dict(batch=4, q_len=1, hq=32, hkv=4, maxp=1024, max_L=16384, sum_L=65536), 16),
     # ragged but short against the share: mean 1000, max 2400 > 2000, share
     # 8 * 64000 / 256 = 2000, 2400 <= 4000: the rule's 1
     ("ragged under two shares", dict(batch=64, q_len=1, hq=32, hkv=8, maxp=150, max_L=2400,
@@ -371,8 +372,8 @@ def test_ragged_hint_plan(lib, name, kw, want):
 #                floor(112861 / 1120) = 100; 100 * 4 = 400; 512 + 400 = 912 < 3584
 #   ragged d128: C = 16 * ceil(416 / 8) = 832; floor(40957 / 832) = 49;
 #                49 * 8 = 392; 256 + 392 = 648 < 2048
-#   long uniform: C = 1184; floor(65536 / 1184) * 4 = 220; 16 + 220 = 236 is
-#                not below 16 * 14 = 224: split-major
+#   long uniform: C = 1024; floor(65536 / 1024) * 4 = 256; 16 + 256 = 272 is
+#                not below 16 * 16 = 256: split-major
 #   cap:         C = 512; floor(65791 / 512) = 128; 256 + 128 < 32768
 #   ragged 32 rows: as ragged d128 (one 32-row block per unit)
 COMPACT_EXTRA = {"ragged d64": 400, "ragged d128": 392, "uniform ~1000": 0, "long uniform": 0,

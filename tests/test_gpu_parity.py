@@ -115,11 +115,12 @@ def test_long_context_bf16_split_sweep(c4, S):
 
 def test_long_context_bf16_bench_path(c4):
     """The call the benchmark times: the planner with the length sum given
-    (a uniform batch: the pages' rule, S = 14, fused combine)."""
+    (a uniform batch: the pages' rule's S = 14 raised to fill the 256 CUs,
+    S = 16, fused combine)."""
     wl, ref = c4
     case("paged bf16 B4 Hq32/Hkv4 d128 L16384, planner with the length sum")
     plan = assert_paged(wl, ref=ref, strict=True, sum_hint=True)
-    assert plan.num_splits == 14 and plan.combine == 2
+    assert plan.num_splits == 16 and plan.combine == 2
 
 
 def test_ragged_fp16_outliers_full_size():
