@@ -103,8 +103,9 @@ typedef struct {
                             * With it, an automatic plan (num_splits 0) also
                             * splits a ragged batch (max_seqlen_k over twice
                             * the mean length) whose longest sequence exceeds
-                            * two compute units' fair shares of all keys,
-                            * into pieces of at most two thirds of a share (an
+                            * one and a half compute units' fair shares of
+                            * all keys, into pieces of at most three fifths of
+                            * a share (an
                             * addition to the pages' rule), raises a split
                             * count above 1 that leaves compute units idle
                             * until the workgroups fill them (another

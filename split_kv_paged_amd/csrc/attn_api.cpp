@@ -79,26 +79,30 @@ int rows_per_block(int64_t rows, int head_dim) {
 // Given the sum of the batch's lengths, a compute unit's fair share of the
 // job is streams * sum / num_cus keys, streams being the KV passes per
 // sequence (head units x row blocks).  In a ragged batch (longest sequence
-// over twice the mean) whose longest sequence also exceeds two shares, that
-// sequence would outlast the rest of the batch on one workgroup, so it is
-// cut into pieces of at most two thirds of a share; shorter sequences keep
-// fewer splits (with the length sum the call launches only the splits that
-// hold keys, see the compact list).  Uniform batches are left to the pages'
-// rule, which already sizes splits by the common length.  Returns the split
-// count this asks for (1 when it does not apply), at most kMaxSplitsRule.
+// over twice the mean) whose longest sequence also exceeds one and a half
+// shares, that sequence would outlast the rest of the batch on one
+// workgroup, so it is cut into pieces of at most three fifths of a share;
+// shorter sequences keep fewer splits (with the length sum the call
+// launches only the splits that hold keys, see the compact list).  Uniform
+// batches are left to the pages' rule, which already sizes splits by the
+// common length.  Returns the split count this asks for (1 when it does not
+// apply), at most kMaxSplitsRule.
 // Measured on MI355X with the compact list (paged, 8 KV heads, lengths
-// log-uniform in 1..8192 or 1..4096), us at half-share pieces -> two-thirds
-// pieces: 128 sequences d 64 54.1 (S 5) -> 53.6 (S 4); 32 sequences d 128
-// 43.0 (S 11) -> 38.1 (S 8); 64 sequences up to 4096 31.4 (S 9) -> 30.0
-// (S 7); 128 sequences d 128 91.5 (S 5) -> 90.1 (S 4); 16 sequences 16.0
-// (S 29) -> 16.1 (S 22).  Unsplit, the first of these takes 76.7 us.
+// log-uniform), us, two shares and two-thirds pieces -> one and a half
+// shares and three-fifths pieces: 128 sequences fp16 d 64 (head pairs,
+// 1..8192) 46.8 (S 7) -> 45.4 (S 8); 32 bf16 d 128 (1..8192) 24.8 (S 14)
+// -> 24.5 (S 15); 128 bf16 d 128 (1..8192; the longest 1.76 shares) 126.0
+// (S 1) -> 100.7 (S 3); 64 up to 4096 and 256 fp16 d 64 up to 4096: the same
+// S and time.  Earlier, on a slower kernel, half-share pieces had lost to
+// two-thirds ones (128 sequences d 64 54.1 -> 53.6 us; 32 sequences d 128
+// 43.0 -> 38.1; 64 up to 4096 31.4 -> 30.0).
 int ragged_splits(int64_t batch, int64_t streams, int64_t sum_seqlen_k, int64_t max_seqlen_k,
                   int num_cus) {
   if (sum_seqlen_k <= 0 || streams <= 0 || batch <= 0) return 1;
   const double mean = double(sum_seqlen_k) / double(batch);
   const double share = double(streams) * double(sum_seqlen_k) / double(num_cus);
-  if (double(max_seqlen_k) <= 2.0 * mean || double(max_seqlen_k) <= 2.0 * share) return 1;
-  const double s = std::ceil(1.5 * double(max_seqlen_k) / share);
+  if (double(max_seqlen_k) <= 2.0 * mean || double(max_seqlen_k) <= 1.5 * share) return 1;
+  const double s = std::ceil(5.0 * double(max_seqlen_k) / (3.0 * share));
   return s >= kMaxSplitsRule ? kMaxSplitsRule : int(s);
 }
 

@@ -325,29 +325,29 @@ def test_check_paged_inputs(lib):
 RAGGED_CASES = [
     # (name, kwargs, expected S)
     # 128 seqs, 16 q heads / 8 KV heads, d 64 as 4 head pairs: share =
-    # 4 * 112861 / 256 = 1763.45; 7769 > 3526.9; ceil(1.5 * 7769 / 1763.45) =
-    # ceil(6.61) = 7; page rule alone: 1
+    # 4 * 112861 / 256 = 1763.45; 7769 > 1.5 * 1763.45 = 2645.2;
+    # ceil(5 * 7769 / (3 * 1763.45)) = ceil(7.34) = 8; page rule alone: 1
     ("ragged d64", dict(batch=128, q_len=1, hq=16, hkv=8, d=64, maxp=512, max_L=7769,
-                        sum_L=112861), 7),
+                        sum_L=112861), 8),
     # 32 seqs GQA-4 d 128: share = 8 * 40957 / 256 = 1279.9;
-    # ceil(1.5 * 6642 / 1279.9) = ceil(7.78) = 8
-    ("ragged d128", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=416, max_L=6642, sum_L=40957), 8),
+    # ceil(5 * 6642 / (3 * 1279.9)) = ceil(8.65) = 9
+    ("ragged d128", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=416, max_L=6642, sum_L=40957), 9),
     # near-uniform lengths: share = 8 * 32002 / 256 = 1000.06; 1100 <= 2000: rule's 1
     ("uniform ~1000", dict(batch=32, q_len=1, hq=32, hkv=8, maxp=69, max_L=1100, sum_L=32002), 1),
     # long uniform context, GQA-8: max_L = mean, not ragged: the rule's 14
     # leaves 256 - 16 * 14 = 32 CUs idle; with the sum, 256 / 16 = 16
     ("long uniform", dict(batch=4, q_len=1, hq=32, hkv=4, maxp=1024, max_L=16384, sum_L=65536), 16),
     # ragged but short against the share: mean 1000, max 2400 > 2000, share
-    # 8 * 64000 / 256 = 2000, 2400 <= 4000: the rule's 1
-    ("ragged under two shares", dict(batch=64, q_len=1, hq=32, hkv=8, maxp=150, max_L=2400,
+    # 8 * 64000 / 256 = 2000, 2400 <= 1.5 * 2000: the rule's 1
+    ("ragged under 1.5 shares", dict(batch=64, q_len=1, hq=32, hkv=8, maxp=150, max_L=2400,
                                      sum_L=64000), 1),
     # one long sequence among 255 one-key ones: share = 65791 / 256 = 257.0,
-    # ceil(1.5 * 65536 / 257.0) = 383 pieces asked, capped at 128
+    # ceil(5 * 65536 / (3 * 257.0)) = 426 pieces asked, capped at 128
     ("cap", dict(batch=256, q_len=1, hq=1, hkv=1, maxp=4096, max_L=65536, sum_L=65536 + 255), 128),
     # 32 query rows per unit (q_len 8, G 4): two row blocks of 16 would be one
     # 32-row block, streams = 8: share = 8 * 40957 / 256, as in "ragged d128"
     ("ragged 32 rows", dict(batch=32, q_len=8, hq=32, hkv=8, maxp=416, max_L=6642,
-                            sum_L=40957), 8),
+                            sum_L=40957), 9),
 ]
 
 
@@ -368,16 +368,16 @@ def test_ragged_hint_plan(lib, name, kw, want):
 
 # Compact list: extra_blocks = max(1, floor(sum / C) * head units * row
 # blocks), used when units + extra_blocks < units * S.  Worked by hand:
-#   ragged d64:  4 head pairs; C = 16 * ceil(486 / 7) = 1120;
-#                floor(112861 / 1120) = 100; 100 * 4 = 400; 512 + 400 = 912 < 3584
-#   ragged d128: C = 16 * ceil(416 / 8) = 832; floor(40957 / 832) = 49;
-#                49 * 8 = 392; 256 + 392 = 648 < 2048
+#   ragged d64:  4 head pairs; C = 16 * ceil(486 / 8) = 976;
+#                floor(112861 / 976) = 115; 115 * 4 = 460; 512 + 460 = 972 < 4096
+#   ragged d128: C = 16 * ceil(416 / 9) = 752; floor(40957 / 752) = 54;
+#                54 * 8 = 432; 256 + 432 = 688 < 2304
 #   long uniform: C = 1024; floor(65536 / 1024) * 4 = 256; 16 + 256 = 272 is
 #                not below 16 * 16 = 256: split-major
 #   cap:         C = 512; floor(65791 / 512) = 128; 256 + 128 < 32768
 #   ragged 32 rows: as ragged d128 (one 32-row block per unit)
-COMPACT_EXTRA = {"ragged d64": 400, "ragged d128": 392, "uniform ~1000": 0, "long uniform": 0,
-                 "ragged under two shares": 0, "cap": 128, "ragged 32 rows": 392}
+COMPACT_EXTRA = {"ragged d64": 460, "ragged d128": 432, "uniform ~1000": 0, "long uniform": 0,
+                 "ragged under 1.5 shares": 0, "cap": 128, "ragged 32 rows": 432}
 
 
 @pytest.mark.parametrize("name,kw,want", RAGGED_CASES, ids=[c[0] for c in RAGGED_CASES])

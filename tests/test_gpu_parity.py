@@ -141,7 +141,7 @@ def test_ragged_fp16_outliers_bench_path():
     case("paged fp16 B128 Hq16/Hkv8 d64 L log-uniform 1..8192, 1%% outliers x8 (%d rows), "
          "planner with the length sum" % wl.meta["outlier_rows"])
     plan = assert_paged(wl, sum_hint=True)
-    assert plan.num_splits == 7 and plan.heads_per_row == 2 and plan.extra_blocks > 0
+    assert plan.num_splits == 8 and plan.heads_per_row == 2 and plan.extra_blocks > 0
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
