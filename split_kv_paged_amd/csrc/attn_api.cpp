@@ -17,6 +17,11 @@ namespace {
 constexpr int kBlockM = 16;         // M tile of the pack rule (MFMA tile height)
 constexpr int kBlockN = 128;        // N tile of the "at most 4 blocks" split rule
 constexpr int kGranule = 16;        // split ranges are multiples of 16 keys
+// Raising a split count to fill the CUs (with the length sum) stops at 16
+// splits (one round of partial loads in the combine) and at kFillKeys keys
+// per split (a 16-key tile for each of the 8 waves).
+constexpr int kFillSplits = 16;
+constexpr int kFillKeys = 128;
 constexpr int kMaxSplitsRule = 128; // candidate split counts tried by the rule
 constexpr int kMaxSplits = 1024;    // largest split count a caller may ask for
 constexpr int kDefaultCus = 256;    // one MI355X
@@ -175,13 +180,14 @@ attn_status make_plan(int64_t batch, int q_len, int hq, int hkv, int head_dim, i
     // With the length sum (a caller that plans on the host), a split count
     // that leaves compute units idle is raised until the workgroups fill
     // them: the rule's 85% slack spares separate combine launches, and the
-    // fused combine here costs about the same at any count up to 16.
-    // Measured on MI355X (bf16 GQA-8, 4 sequences of 16384 keys, 16 units):
-    // the rule's S = 14 (224 workgroups) 26.05-26.09 us, S = 16 (256)
-    // 25.51-25.55.
+    // fused combine here costs about the same at any count up to 16 (one
+    // round of loads), as long as each split keeps a tile for each of the
+    // 8 waves.  Measured on MI355X (bf16 GQA-8, 4 sequences of 16384 keys,
+    // 16 units): the rule's S = 14 (224 workgroups) 26.05-26.09 us, S = 16
+    // (256) 25.51-25.55.
     if (sum_seqlen_k > 0 && splits > 1 && total * splits < num_cus) {
       const int64_t fill = std::min<int64_t>(
-          {int64_t(num_cus) / total, int64_t(kMaxSplitsRule), ceil_div(max_seqlen_k, kGranule)});
+          {int64_t(num_cus) / total, int64_t(kFillSplits), max_seqlen_k / kFillKeys});
       if (fill > splits) splits = int(fill);
     }
   }

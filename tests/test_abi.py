@@ -404,6 +404,33 @@ def test_compact_list_plan(lib, name, kw, want):
         assert L.STATUS[code2] == "ATTN_OK" and plan2.extra_blocks == 0
 
 
+FILL_CASES = [
+    # (name, kwargs, S with the sum, S of the pages' rule)
+    # 16 units (4 x 4 KV heads): 14 * 16 = 224 < 256 CUs; 256 / 16 = 16
+    ("long context", dict(batch=4, q_len=1, hq=32, hkv=4, maxp=1024, max_L=16384), 16, 14),
+    # 16 units again, 4000 keys: 4000 / 128 = 31 keys-wise, so 16
+    ("two sequences", dict(batch=2, q_len=1, hq=32, hkv=8, maxp=250, max_L=4000), 16, 14),
+    # 8 units, 1000 keys: 256 / 8 = 32, but 1000 / 128 = 7 tiles of 8 waves: stays 7
+    ("short", dict(batch=1, q_len=1, hq=32, hkv=8, maxp=63, max_L=1000), 7, 7),
+    # 4 units, 65536 keys: 64 asked by the CUs, capped at 16 (one round of loads)
+    ("cap 16", dict(batch=1, q_len=1, hq=32, hkv=4, maxp=4096, max_L=65536), 16, None),
+]
+
+
+@pytest.mark.parametrize("name,kw,want,rule", FILL_CASES, ids=[c[0] for c in FILL_CASES])
+def test_fill_the_cus_with_the_sum(lib, name, kw, want, rule):
+    """With the length sum (uniform lengths here), a split count that leaves
+    CUs idle is raised to fill them, up to 16 splits and down to 128 keys a
+    split; without it the plan is the pages' rule."""
+    code, plan = _plan(lib, **dict(kw, sum_L=kw["batch"] * kw["max_L"]))
+    assert L.STATUS[code] == "ATTN_OK"
+    code0, plan0 = _plan(lib, **kw)
+    assert L.STATUS[code0] == "ATTN_OK"
+    if rule is not None:
+        assert plan0.num_splits == rule
+    assert plan.num_splits == max(want, plan0.num_splits)
+
+
 def test_ragged_hint_rejects_out_of_range(lib):
     base = dict(batch=4, q_len=1, hq=8, hkv=2, maxp=64, max_L=1000)
     assert L.STATUS[_plan(lib, **base, sum_L=-1)[0]] == "ATTN_ERR_SHAPE"
