@@ -40,7 +40,10 @@
 //
 // Packed query rows beyond the unit's real rows are zero; their lanes do the
 // same (SIMD) work and are never written.  A workgroup carries one, two or
-// four 16-row blocks (NRB) of one unit.
+// four 16-row blocks (NRB) of one unit.  Units are placed on the XCDs by
+// where their slices sit in the key rows (see the work lists below), and
+// the launch-invariant integer divisions of the index arithmetic are
+// multiply-high-and-shift sequences prepared on the host.
 //
 // Sources: attention definition (SmallQ FlashAttention README, section 接口);
 // online softmax with max offset (ai6s.net FlashAttention article, section
