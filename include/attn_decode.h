@@ -160,7 +160,9 @@ typedef struct {
                              /* (16-byte loads, head_dim a multiple of 8 below */
                              /* the tile's), 30000 (element loads) or 40000    */
                              /* (head groups) + 1000 if paged + tile head dim */
-                             /* (32, 64, 128 or 256)                          */
+                             /* (32, 64, 128 or 256); + 100000 in the record  */
+                             /* of a kvcache call whose split kernel wrote    */
+                             /* the new keys itself (no separate append)      */
     int32_t split_keys;      /* C: split s covers keys [s*C, (s+1)*C) of every */
                              /* sequence, C = 16*ceil(ceil(max_seqlen_k/16)/S) */
     int32_t heads_per_row;   /* KV heads per unit: 1, or R = 2 (head_dim 64) */
@@ -260,7 +262,17 @@ attn_status attn_decode_fwd_noalloc(const attn_decode_shape* shape, const void* 
  *                 new_len - 1 of k_cache / v_cache (the block table must map
  *                 those pages), then attention covers L_b = cache_seqlens[b]
  *                 + new_len keys.  cache_seqlens itself is not changed.
- *                 shape->max_seqlen_k must bound every L_b.
+ *                 shape->max_seqlen_k must bound every L_b.  With at most
+ *                 4 new keys per sequence on the kernels whose tiles go
+ *                 straight to LDS (head_dim a multiple of 8 from 40 to
+ *                 256, or head groups) and no varlen queries, the
+ *                 attention kernel writes them itself and reads them from
+ *                 k_new / v_new (one launch; the record of attn_last_plan
+ *                 then has kernel + 100000), unless that would lower the
+ *                 workgroups resident per CU of a grid larger than one
+ *                 round; otherwise an append kernel runs first.  Either
+ *                 way the cache ends the same, and keys past the block
+ *                 table are not written.
  *   causal        0: every query row sees all L_b keys.  1: query i of q_len
  *                 sees keys j <= L_b - q_len + i (the queries are the last
  *                 q_len positions: bottom-right alignment); a row that sees

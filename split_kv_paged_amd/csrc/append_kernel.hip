@@ -7,6 +7,8 @@
 // MixedQuantSparseFlashMla article, section 参数说明), before attention
 // reads the cache.  One workgroup per (sequence, new key) copies the Hkv
 // rows of K and V; the data is small, so 16-bit element copies are enough.
+// The split kernel writes up to kMaxFusedNew keys a sequence itself where it
+// can (split_mfma.hip); this kernel covers the other calls.
 #include "internal.h"
 
 namespace skv {

@@ -114,7 +114,9 @@ int ragged_splits(int64_t batch, int64_t streams, int64_t sum_seqlen_k, int64_t 
 // Diagnostic kernel id: 10000 (16-byte loads), 20000 (16-byte loads with a
 // column mask: head_dim a multiple of 8), 30000 (element loads: any other
 // head_dim) or 40000 (head groups) + 1000 if paged + the tile head dim
-// (32/64/128/256).
+// (32/64/128/256).  A forward call whose split kernel also wrote the
+// appended keys records kAppendedInKernel more.
+constexpr int kAppendedInKernel = 100000;
 int kernel_id(int head_dim, bool paged, bool grouped) {
   if (grouped) return 40000 + 1000 + 128;
   const bool exact = head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
@@ -322,7 +324,8 @@ WsView caller_workspace(const attn_plan& plan, int64_t nrows, int head_dim, void
 // Launch the split kernel (which merges the splits itself when S > 1).
 attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dtype, int head_dim,
                 void* out, float* lse, const WsView& ws, hipStream_t stream,
-                int64_t max_seqlen_k = 0, int64_t sum_seqlen_k = 0) {
+                int64_t max_seqlen_k = 0, int64_t sum_seqlen_k = 0,
+                const skv::AppendParams* append = nullptr) {
   const int S = plan.num_splits;
   prm.num_splits = S;
   prm.split_keys = plan.split_keys;
@@ -351,9 +354,12 @@ attn_status run(const attn_plan& plan, skv::SplitParams prm, bool paged, int dty
                   max_seqlen_k >= skv::kMinRankKeys &&
                   (sum_seqlen_k <= 0 || sum_seqlen_k >= int64_t(skv::kMinRankMean) * prm.batch);
   prm.extra_blocks = paged ? plan.extra_blocks : 0;
-  if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream) != hipSuccess)
+  bool in_kernel = false;
+  if (skv::launch_split_mfma(dtype, paged, prm, plan.grid, stream, append, &in_kernel) !=
+      hipSuccess)
     return ATTN_ERR_HIP;
   g_last_plan = plan;
+  if (in_kernel) g_last_plan.kernel += kAppendedInKernel;
   g_have_last = true;
   return ATTN_OK;
 }
@@ -453,8 +459,11 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
   p.total_q = total_q;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(D));
   p.scale_log2 = scale * 1.4426950408889634074f;
-  if (new_len > 0) {  // the new keys go into the cache first, on the same stream
-    skv::AppendParams a{};
+  // The new keys go into the cache before attention reads them: written by
+  // the split kernel itself where it can, else by the append kernel first on
+  // the same stream.
+  skv::AppendParams a{};
+  if (new_len > 0) {
     a.k_new = k_new;
     a.v_new = v_new;
     a.k_cache = k_cache;
@@ -467,10 +476,10 @@ attn_status decode_common(const attn_decode_shape* shape, const void* q, void* k
     a.head_dim = D;
     a.page_size = shape->page_size;
     a.max_pages = shape->max_pages_per_seq;
-    if (skv::launch_append(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+    a.num_cus = cus;
   }
   return run(plan, p, true, shape->dtype, D, out, lse, wsv, static_cast<hipStream_t>(stream),
-             shape->max_seqlen_k, shape->sum_seqlen_k);
+             shape->max_seqlen_k, shape->sum_seqlen_k, new_len > 0 ? &a : nullptr);
 }
 
 }  // namespace

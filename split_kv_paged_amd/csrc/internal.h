@@ -68,11 +68,20 @@ struct SplitParams {
   // page_size, split_keys and (head groups) the query heads per KV head,
   // heads_per_unit * head_dim / 128.
   FastDiv fd_units, fd_unit_heads, fd_group, fd_hpu, fd_page, fd_split_keys, fd_gq;
+  // Set by launch_split_mfma for an appending launch (paged, direct-to-LDS
+  // tiles), else null: the seq_add keys [batch, seq_add, Hkv, head_dim] that
+  // the split kernel itself writes into the cache.
+  const void* k_new;
+  const void* v_new;
 };
 
 // Append new_len keys per sequence to the paged cache (before attention):
 // k_new/v_new [batch, new_len, Hkv, head_dim] go to key positions
 // seqlens[b] .. seqlens[b] + new_len - 1.
+// At most this many keys per sequence are appended by the split kernel
+// itself; longer appends (and the register-ring kernels, and varlen calls)
+// run the append kernel first.
+constexpr int kMaxFusedNew = 4;
 struct AppendParams {
   const void* k_new;
   const void* v_new;
@@ -81,6 +90,7 @@ struct AppendParams {
   const int32_t* block_table;
   const int32_t* seqlens;
   int batch, new_len, hkv, head_dim, page_size, max_pages;
+  int num_cus;  // of the device (whether the split kernel's appending copy fits)
 };
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
@@ -125,8 +135,12 @@ struct CombineParams {
 
 // Split kernel (split_mfma.hip): 16 packed rows per workgroup, fused
 // combine when num_splits > 1; p.head_dim in [1, 256].
+// append (may be null): keys to write into the paged cache before attention
+// reads it, either by the split kernel itself (then *in_kernel = true) or by
+// the append kernel first.
 hipError_t launch_split_mfma(int dtype, bool paged, const SplitParams& p, int grid,
-                             hipStream_t s);
+                             hipStream_t s, const AppendParams* append = nullptr,
+                             bool* in_kernel = nullptr);
 hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t s);
 
 }  // namespace skv

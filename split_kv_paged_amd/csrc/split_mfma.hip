@@ -193,8 +193,9 @@ __device__ __forceinline__ float from_lane(float x, int src_lane) {
 // NRB: 16-row blocks a workgroup carries (1; 2 or 4 when a unit has more
 // than 16 or 32 packed rows, so its KV is read once for up to 64 rows).
 // tid: the thread index (passed in so that the compact list's loop can
-// hide it from loop-invariant hoisting).
-template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB>
+// hide it from loop-invariant hoisting).  APP: this launch also appends
+// p.seq_add keys per sequence from p.k_new / p.v_new (see below).
+template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB, bool APP>
 __device__ __forceinline__ void split_unit(const SplitParams& p, const int split, const int b,
                                            const int uh, const int rb, const int tid) {
   using M = Mf<DT>;
@@ -319,6 +320,16 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   if (split >= nsplit) return;
   const bool direct = nsplit == 1;
   const int t1 = min(t0 + p.split_keys, L);
+  // Keys appended by this call (k_new set; paged calls whose tiles go
+  // straight to LDS): the last seq_add keys, [Lc, L), are read from k_new /
+  // v_new [batch, seq_add, Hkv, head_dim] rather than from the cache, and
+  // one workgroup of the KV head (row block 0, the first query head of its
+  // group) writes them into the cache for later calls.  No workgroup of
+  // this launch reads those cache rows, so no ordering between workgroups
+  // is needed.
+  constexpr bool fused = APP;
+  static_assert(!APP || (PAGED && kDma), "appending launches: paged, direct-to-LDS tiles");
+  const int Lc = fused ? L - p.seq_add : L;  // keys already in the cache
   const int n_tiles = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
@@ -568,11 +579,60 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   constexpr int kCPR = ROWB / 16;    // 16-byte chunks per staged row
   constexpr int kRPI = 1024 / ROWB;  // rows per load instruction
   typedef __attribute__((address_space(3))) void* lds_ptr;
+  // The appended keys of a tile (at most kMaxFusedNew rows): lane l holds
+  // chunk l % kCPR of new row j * kNewPer + l / kCPR, fetched from k_new /
+  // v_new with the tile's cache rows and put into the slot when it lands.
+  constexpr int kNewPer = 64 / kCPR;
+  constexpr int kNewPass = (kMaxFusedNew + kNewPer - 1) / kNewPer;
+  uint4 nk[fused ? kNewPass : 1] = {}, nv[fused ? kNewPass : 1] = {};
+  auto new_key = [&](int tt, int j) -> int {  // key of this lane's row j, or -1
+    const int key = max(tt, Lc) + j * kNewPer + lane / kCPR;
+    return key < min(tt + kTile, t1) && (GEN == 0 || (lane % kCPR) * 8 < kvd) ? key : -1;
+  };
+  auto fetch_new = [&](int tt) {
+    const uint16_t* kn = static_cast<const uint16_t*>(p.k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(p.v_new);
+#pragma unroll
+    for (int j = 0; j < kNewPass; ++j) {
+      const int key = new_key(tt, j);
+      if (key >= 0) {
+        const long src = ((long)(b * p.seq_add + key - Lc) * p.hkv + h) * kvd + (lane % kCPR) * 8;
+        nk[j] = *reinterpret_cast<const uint4*>(kn + src);
+        nv[j] = *reinterpret_cast<const uint4*>(vn + src);
+      }
+    }
+  };
+  auto put_new = [&](int idx, int page, bool writer) {
+    const int tt = t0 + (wave + idx * NW) * kTile;
+    uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(p.k));
+    uint16_t* vc = static_cast<uint16_t*>(const_cast<void*>(p.v));
+    const long row0 = tile_row0(idx, page);
+#pragma unroll
+    for (int j = 0; j < kNewPass; ++j) {
+      const int key = new_key(tt, j);
+      if (key >= 0) {
+        const int r = key - tt, c = lane % kCPR;
+        const int off = r * ROWB + ((c ^ swz(r)) * 16);
+        *reinterpret_cast<uint4*>(my_k + off) = nk[j];
+        *reinterpret_cast<uint4*>(my_v + off) = nv[j];
+        if (writer && key < p.max_pages * p.page_size) {
+          const long dst = row0 + (long)r * row_stride + c * 8;
+          *reinterpret_cast<uint4*>(kc + dst) = nk[j];
+          *reinterpret_cast<uint4*>(vc + dst) = nv[j];
+        }
+      }
+    }
+  };
   auto issue_dma = [&](int idx, int page) {
     page = __builtin_amdgcn_readfirstlane(page);
     const int tt = t0 + (wave + idx * NW) * kTile;
     const long row0 = tile_row0(idx, page);
-    const uint32_t bytes = uint32_t(min(kTile, t1 - tt) * row_stride * 2);
+    // rows past the cached keys read as zero; appended ones come from k_new
+    const uint32_t bytes =
+        uint32_t((fused ? max(0, min(kTile, min(t1, Lc) - tt)) : min(kTile, t1 - tt)) * row_stride * 2);
+    if constexpr (fused) {
+      if (tt + kTile > Lc) fetch_new(tt);
+    }
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0, bytes);
 #pragma unroll
@@ -597,6 +657,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
     // the page ids alone, not for the query rows loaded after them.
     if (my_tiles > 0) issue_dma(0, __builtin_amdgcn_readlane(pages, 0));
     load_q();
+    const bool writer = fused && rb == 0 && hq0 % p.group == 0;
     for (int cb = 0; cb < my_tiles; cb += 64) {
       auto page_at = [&](int i) { return __builtin_amdgcn_readlane(pages, i); };
       if (cb > 0) {
@@ -606,6 +667,9 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
       const int n = min(64, my_tiles - cb);
       for (int i = 0; i < n; ++i) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);  // tile i has landed in the slot
+        if constexpr (fused) {
+          if (t0 + (wave + (cb + i) * NW) * kTile + kTile > Lc) put_new(cb + i, page_at(i), writer);
+        }
         uint4 kq[KB];
         uint2 vt[DB];
 #pragma unroll
@@ -861,7 +925,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
 // slices, no head pairs) 51.7 -> 51.2.  Otherwise j = i.
 // EXTRA: a kernel built for the compact list (its loop over items costs
 // about ten VGPRs, so the split-major kernels are built without it).
-template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB, bool EXTRA>
+template <int DT, int D, int NW, int NBUF, bool PAGED, int GEN, int NRB, bool EXTRA, bool APP>
 __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p) {
   static_assert(PAGED || !EXTRA, "the compact list is for paged calls");
   __shared__ __attribute__((aligned(16))) int s_seq[kMaxOrderBatch + 1];
@@ -913,7 +977,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
       const int rem = r % per_seq;
-      split_unit<DT, D, NW, NBUF, PAGED, GEN, NRB>(p, 1 + r / per_seq, bs, rem % p.unit_heads,
+      split_unit<DT, D, NW, NBUF, PAGED, GEN, NRB, APP>(p, 1 + r / per_seq, bs, rem % p.unit_heads,
                                                   rem / p.unit_heads, tid);
       __syncthreads();  // the unit's LDS is reused by the next one
     }
@@ -978,7 +1042,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
     __syncthreads();
     b = __builtin_amdgcn_readfirstlane(s_pick);
   }
-  split_unit<DT, D, NW, NBUF, PAGED, GEN, NRB>(p, split, b, uh, rb, threadIdx.x);
+  split_unit<DT, D, NW, NBUF, PAGED, GEN, NRB, APP>(p, split, b, uh, rb, threadIdx.x);
 }
 
 // Waves per workgroup: 8 up to D = 128, 4 at D = 256 (accumulators and
@@ -989,21 +1053,67 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 // 28.2 vs 27.4 us; with 32 query rows per unit (causal q_len 8): 37.2 vs
 // 34.7 us.  Direct-to-LDS with 16 waves, or two tiles per wave step, was
 // slower (28.2 and 28.1 us).
+// Workgroups of a kernel resident per CU (looked up once per kernel).
+template <auto K>
+int resident(int nw) {
+  static const int n = [nw] {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(K),
+                                                     nw * 64, 0) != hipSuccess)
+      return 0;
+    return blocks;
+  }();
+  return n;
+}
+
 template <int DT, int D, bool PAGED, int GEN, int NRB>
-hipError_t launch_mfma_k(const SplitParams& p, int grid, hipStream_t s) {
+hipError_t launch_mfma_k(const SplitParams& prm, int grid, hipStream_t s,
+                         const AppendParams* append, bool* in_kernel) {
   constexpr bool kDirect = GEN != 2 && D >= 64;
   constexpr int NW = D <= 128 ? 8 : 4;
   constexpr int NBUF = kDirect ? 0 : D >= 128 ? 1 : 2;
+  // Appended keys: a direct-to-LDS kernel takes a few per sequence itself
+  // (one launch instead of two) where its appending copy keeps the plain
+  // one's resident workgroups, or the grid fits in one round of them;
+  // otherwise the append kernel runs first.
+  if (append && append->new_len > 0) {
+    if constexpr (kDirect && PAGED) {
+      if (append->new_len <= kMaxFusedNew && !prm.cu_q) {
+        const bool ex = prm.extra_blocks > 0;
+        const int plain = ex ? resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, false>>(NW)
+                             : resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, false>>(NW);
+        const int fused = ex ? resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, true>>(NW)
+                             : resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, true>>(NW);
+        if (fused > 0 && (fused >= plain || grid <= (long)fused * append->num_cus)) {
+          SplitParams p = prm;
+          p.k_new = append->k_new;
+          p.v_new = append->v_new;
+          if (ex)
+            hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, true>),
+                               dim3(grid), dim3(NW * 64), 0, s, p);
+          else
+            hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, true>),
+                               dim3(grid), dim3(NW * 64), 0, s, p);
+          if (in_kernel) *in_kernel = true;
+          return hipGetLastError();
+        }
+      }
+    }
+    const hipError_t e = launch_append(*append, s);
+    if (e != hipSuccess) return e;
+  }
+  SplitParams p = prm;
+  p.k_new = p.v_new = nullptr;
   if (p.extra_blocks > 0) {
     if constexpr (PAGED) {
-      hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true>), dim3(grid),
-                         dim3(NW * 64), 0, s, p);
+      hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, false>),
+                         dim3(grid), dim3(NW * 64), 0, s, p);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false>), dim3(grid),
-                     dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, false>),
+                     dim3(grid), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1011,44 +1121,46 @@ hipError_t launch_mfma_k(const SplitParams& p, int grid, hipStream_t s) {
 // kernels at head dims 64 and 128 (the planner asks for them only there);
 // four at 128 read Q from LDS.
 template <int DT, int D, bool PAGED, int GEN>
-hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s) {
+hipError_t launch_mfma_d(const SplitParams& p, int grid, hipStream_t s, const AppendParams* a,
+                         bool* ik) {
   if constexpr (GEN == 0 && (D == 64 || D == 128)) {
-    if (p.nrb == 2) return launch_mfma_k<DT, D, PAGED, GEN, 2>(p, grid, s);
+    if (p.nrb == 2) return launch_mfma_k<DT, D, PAGED, GEN, 2>(p, grid, s, a, ik);
   }
   if constexpr (GEN == 0 && (D == 64 || D == 128)) {
-    if (p.nrb == 4) return launch_mfma_k<DT, D, PAGED, GEN, 4>(p, grid, s);
+    if (p.nrb == 4) return launch_mfma_k<DT, D, PAGED, GEN, 4>(p, grid, s, a, ik);
   }
   if (p.nrb != 1) return hipErrorInvalidValue;
-  return launch_mfma_k<DT, D, PAGED, GEN, 1>(p, grid, s);
+  return launch_mfma_k<DT, D, PAGED, GEN, 1>(p, grid, s, a, ik);
 }
 
 template <int DT, bool PAGED>
-hipError_t launch_mfma_dt(const SplitParams& p, int grid, hipStream_t s) {
+hipError_t launch_mfma_dt(const SplitParams& p, int grid, hipStream_t s, const AppendParams* a,
+                          bool* ik) {
   const int d = p.head_dim;
   if (p.head_group > 1) {  // 2 head-dim-64 or 4 head-dim-32 KV heads per 128-wide row
     if constexpr (PAGED) {
       if (p.head_group * d == 128 && p.nrb == 1)
-        return launch_mfma_k<DT, 128, PAGED, 3, 1>(p, grid, s);
+        return launch_mfma_k<DT, 128, PAGED, 3, 1>(p, grid, s, a, ik);
     }
     return hipErrorInvalidValue;
   }
   switch (d) {
-    case 32: return launch_mfma_d<DT, 32, PAGED, 0>(p, grid, s);
-    case 64: return launch_mfma_d<DT, 64, PAGED, 0>(p, grid, s);
-    case 128: return launch_mfma_d<DT, 128, PAGED, 0>(p, grid, s);
-    case 256: return launch_mfma_d<DT, 256, PAGED, 0>(p, grid, s);
+    case 32: return launch_mfma_d<DT, 32, PAGED, 0>(p, grid, s, a, ik);
+    case 64: return launch_mfma_d<DT, 64, PAGED, 0>(p, grid, s, a, ik);
+    case 128: return launch_mfma_d<DT, 128, PAGED, 0>(p, grid, s, a, ik);
+    case 256: return launch_mfma_d<DT, 256, PAGED, 0>(p, grid, s, a, ik);
   }
   if (d % 8 == 0) {  // rows stay 16-byte aligned
-    if (d <= 32) return launch_mfma_d<DT, 32, PAGED, 1>(p, grid, s);
-    if (d <= 64) return launch_mfma_d<DT, 64, PAGED, 1>(p, grid, s);
-    if (d <= 128) return launch_mfma_d<DT, 128, PAGED, 1>(p, grid, s);
-    if (d <= 256) return launch_mfma_d<DT, 256, PAGED, 1>(p, grid, s);
+    if (d <= 32) return launch_mfma_d<DT, 32, PAGED, 1>(p, grid, s, a, ik);
+    if (d <= 64) return launch_mfma_d<DT, 64, PAGED, 1>(p, grid, s, a, ik);
+    if (d <= 128) return launch_mfma_d<DT, 128, PAGED, 1>(p, grid, s, a, ik);
+    if (d <= 256) return launch_mfma_d<DT, 256, PAGED, 1>(p, grid, s, a, ik);
     return hipErrorInvalidValue;
   }
-  if (d <= 32) return launch_mfma_d<DT, 32, PAGED, 2>(p, grid, s);
-  if (d <= 64) return launch_mfma_d<DT, 64, PAGED, 2>(p, grid, s);
-  if (d <= 128) return launch_mfma_d<DT, 128, PAGED, 2>(p, grid, s);
-  if (d <= 256) return launch_mfma_d<DT, 256, PAGED, 2>(p, grid, s);
+  if (d <= 32) return launch_mfma_d<DT, 32, PAGED, 2>(p, grid, s, a, ik);
+  if (d <= 64) return launch_mfma_d<DT, 64, PAGED, 2>(p, grid, s, a, ik);
+  if (d <= 128) return launch_mfma_d<DT, 128, PAGED, 2>(p, grid, s, a, ik);
+  if (d <= 256) return launch_mfma_d<DT, 256, PAGED, 2>(p, grid, s, a, ik);
   return hipErrorInvalidValue;
 }
 
@@ -1064,8 +1176,8 @@ FastDiv make_fastdiv(uint32_t d) {
 }
 
 hipError_t launch_split_mfma(int dtype, bool paged, const SplitParams& prm, int grid,
-                             hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+                             hipStream_t s, const AppendParams* append, bool* in_kernel) {
+  if (grid <= 0) return append && append->new_len > 0 ? launch_append(*append, s) : hipSuccess;
   SplitParams p = prm;
   auto pos = [](long v) { return uint32_t(v > 1 ? v : 1); };
   p.fd_units = make_fastdiv(pos((long)p.batch * p.unit_heads * p.row_blocks));
@@ -1076,8 +1188,10 @@ hipError_t launch_split_mfma(int dtype, bool paged, const SplitParams& prm, int 
   p.fd_split_keys = make_fastdiv(pos(p.split_keys));
   p.fd_gq = make_fastdiv(pos(p.head_group > 1 ? (long)p.heads_per_unit * p.head_dim / 128 : 1));
   if (paged)
-    return dtype == 1 ? launch_mfma_dt<1, true>(p, grid, s) : launch_mfma_dt<0, true>(p, grid, s);
-  return dtype == 1 ? launch_mfma_dt<1, false>(p, grid, s) : launch_mfma_dt<0, false>(p, grid, s);
+    return dtype == 1 ? launch_mfma_dt<1, true>(p, grid, s, append, in_kernel)
+                      : launch_mfma_dt<0, true>(p, grid, s, append, in_kernel);
+  return dtype == 1 ? launch_mfma_dt<1, false>(p, grid, s, append, in_kernel)
+                    : launch_mfma_dt<0, false>(p, grid, s, append, in_kernel);
 }
 
 }  // namespace skv

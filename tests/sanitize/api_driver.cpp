@@ -18,7 +18,10 @@
 
 namespace skv {
 hipError_t launch_append(const AppendParams&, hipStream_t) { std::abort(); }
-hipError_t launch_split_mfma(int, bool, const SplitParams&, int, hipStream_t) { std::abort(); }
+hipError_t launch_split_mfma(int, bool, const SplitParams&, int, hipStream_t, const AppendParams*,
+                             bool*) {
+  std::abort();
+}
 hipError_t launch_combine(int, const CombineParams&, hipStream_t) { std::abort(); }
 hipError_t scratch_device_address(void**) { std::abort(); }
 }  // namespace skv

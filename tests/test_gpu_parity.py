@@ -332,6 +332,66 @@ def test_kv_append_then_attend(causal, S):
     assert np.array_equal(old.cpu().numpy(), np.array(lens, dtype=np.int32))
 
 
+APPEND_CASES = [
+    # name, dtype, B, q_len, Hq, Hkv, d, old lengths, new_len, S, pack_gqa, length sum,
+    # causal, appended by the attention kernel itself (None: either)
+    ("one key, page edges", "bf16", 8, 1, 32, 8, 128,
+     [0, 15, 16, 17, 31, 500, 1023, 1100], 1, 0, -1, False, False, True),
+    ("four keys, causal, split edges", "fp16", 6, 4, 16, 4, 128,
+     [398, 399, 400, 797, 1195, 3], 4, 3, -1, False, True, True),
+    ("head pairs", "fp16", 8, 1, 16, 8, 64, [0, 1, 63, 64, 200, 777, 1500, 2047], 2, 1, -1,
+     True, False, True),
+    # the compact list's appending copy holds one workgroup per CU against
+    # two: a grid of more than 256 workgroups keeps the append kernel
+    ("head pairs, compact list", "fp16", 8, 1, 16, 8, 64, [0, 1, 63, 64, 200, 777, 1500, 2047],
+     2, 0, -1, True, False, False),
+    ("unpacked heads", "bf16", 4, 1, 32, 8, 128, [5, 700, 31, 1024], 3, 2, 0, False, False, True),
+    ("two row blocks", "bf16", 2, 4, 64, 2, 128, [600, 95], 4, 0, -1, False, True, True),
+    ("head dim 80", "fp16", 4, 1, 8, 2, 80, [14, 300, 0, 999], 1, 0, -1, False, False, True),
+    ("head dim 256", "bf16", 4, 2, 8, 4, 256, [30, 1, 640, 257], 3, 2, -1, False, True, True),
+    ("five keys: append kernel", "bf16", 4, 1, 32, 8, 128, [14, 300, 0, 999], 5, 0, -1,
+     False, False, False),
+    ("head dim 32: append kernel", "fp16", 4, 1, 8, 2, 32, [14, 300, 0, 999], 2, 0, -1,
+     False, False, False),
+    ("compact list", "fp16", 48, 1, 16, 8, 64,
+     [int(x) for x in np.random.default_rng(7).integers(1, 3000, 48)], 1, 0, -1, True, False,
+     None),
+]
+
+
+@pytest.mark.parametrize("spec", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_kv_append_paths(spec):
+    """Appended keys either written by the attention kernel itself (read
+    from k_new / v_new, one launch) or by the append kernel first: outputs
+    match the oracle on the whole cache, and the cache afterwards holds the
+    new rows and nothing else changed."""
+    name, dt, B, qlen, hq, hkv, d, lens, new_len, S, pack, use_sum, causal, in_kernel = spec
+    wl, k_new, v_new, kc_h, vc_h = _append_case(1400 + len(lens) + d, dt, B, qlen, hq, hkv, d,
+                                                lens, new_len)
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    case("append %s: %s B=%d q_len=%d Hq=%d Hkv=%d d=%d new=%d S=%d pack=%d causal=%s"
+         % (name, dt, B, qlen, hq, hkv, d, new_len, S, pack, causal))
+    kc, vc = to_dev(kc_h, dt), to_dev(vc_h, dt)
+    old = i32_dev(np.array(lens, dtype=np.int32))
+    total = int(sum(lens)) + B * new_len
+    out, lse = api.decode_fwd(to_dev(wl.q, dt), kc, vc, i32_dev(wl.block_table), old,
+                              num_splits=S, pack_gqa=pack, softmax_scale=wl.scale,
+                              max_seqlen_k=max(lens) + new_len, k_new=to_dev(k_new, dt),
+                              v_new=to_dev(v_new, dt), causal=causal,
+                              sum_seqlen_k=total if use_sum else None)
+    torch.cuda.synchronize()
+    plan = api.last_plan()
+    print("  plan S=%d heads_per_row=%d extra=%d kernel=%d" % (
+        plan.num_splits, plan.heads_per_row, plan.extra_blocks, plan.kernel), flush=True)
+    if in_kernel is not None:
+        assert (plan.kernel >= 100000) == in_kernel, plan.kernel
+    check_out(bits_of(out), ref_o, dt)
+    check_lse(lse.cpu().numpy(), ref_l)
+    assert np.array_equal(bits_of(kc), wl.k_cache) and np.array_equal(bits_of(vc), wl.v_cache)
+    assert np.array_equal(old.cpu().numpy(), np.array(lens, dtype=np.int32))
+
+
 # ---------------------------------------------------------- ragged splits ----
 
 @pytest.mark.parametrize("lens", [
