@@ -604,6 +604,7 @@ __device__ __forceinline__ void split_unit(const SplitParams& p, const int split
   };
   auto put_new = [&](int idx, int page, bool writer) {
     const int tt = t0 + (wave + idx * NW) * kTile;
+    // the appending entry point takes a writable cache (k_cache, v_cache)
     uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(p.k));
     uint16_t* vc = static_cast<uint16_t*>(const_cast<void*>(p.v));
     const long row0 = tile_row0(idx, page);
@@ -1053,7 +1054,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_split_kernel(const SplitParams p
 // 28.2 vs 27.4 us; with 32 query rows per unit (causal q_len 8): 37.2 vs
 // 34.7 us.  Direct-to-LDS with 16 waves, or two tiles per wave step, was
 // slower (28.2 and 28.1 us).
-// Workgroups of a kernel resident per CU (looked up once per kernel).
+// Workgroups of a kernel resident per CU (looked up once per kernel, on the
+// first GPU that launches it: every GPU of a process is taken to be alike).
 template <auto K>
 int resident(int nw) {
   static const int n = [nw] {
