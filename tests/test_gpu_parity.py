@@ -1122,3 +1122,35 @@ def test_seeded_mixture_with_length_sum(k):
     e2 = check_lse(lse.cpu().numpy(), ref_l)
     print("  plan S=%d heads_per_row=%d extra_blocks=%d max|dO|=%.3g max|dLSE|=%.3g" % (
         plan.num_splits, plan.heads_per_row, plan.extra_blocks, e1, e2), flush=True)
+
+
+@pytest.mark.parametrize("k", range(48, 72))
+def test_seeded_mixture_with_appends(k):
+    """More of the seeded mixture as kvcache calls: 1 to 5 new keys a
+    sequence (written by the attention launch itself or by the append kernel
+    first, whichever the call takes), the length sum on every other call.
+    Outputs match the oracle over the whole cache and the cache afterwards
+    holds the new rows, byte for byte."""
+    dt, d, hkv, G, qlen, causal, B, lens, _, S = _random_config(k)
+    new_len = 1 + k % 5
+    wl, k_new, v_new, kc_h, vc_h = _append_case(9200 + k, dt, B, qlen, hkv * G, hkv, d, lens,
+                                                new_len)
+    case("mixture %d with %d new keys: %s d%d Hkv%d G%d q%d causal=%s B%d L=%s S=%d"
+         % (k, new_len, dt, d, hkv, G, qlen, causal, B, lens, S))
+    ref_o, ref_l = oracle.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                          wl.cache_seqlens, dt, scale=wl.scale, causal=causal)
+    kc, vc = to_dev(kc_h, dt), to_dev(vc_h, dt)
+    total = int(sum(lens)) + B * new_len
+    out, lse = api.decode_fwd(to_dev(wl.q, dt), kc, vc, i32_dev(wl.block_table),
+                              i32_dev(np.array(lens, dtype=np.int32)), num_splits=S,
+                              softmax_scale=wl.scale, max_seqlen_k=max(lens) + new_len,
+                              k_new=to_dev(k_new, dt), v_new=to_dev(v_new, dt), causal=causal,
+                              sum_seqlen_k=total if k % 2 else None)
+    torch.cuda.synchronize()
+    plan = api.last_plan()
+    e1 = check_out(bits_of(out), ref_o, dt)
+    e2 = check_lse(lse.cpu().numpy(), ref_l)
+    print("  plan S=%d heads_per_row=%d extra_blocks=%d kernel=%d max|dO|=%.3g max|dLSE|=%.3g"
+          % (plan.num_splits, plan.heads_per_row, plan.extra_blocks, plan.kernel, e1, e2),
+          flush=True)
+    assert np.array_equal(bits_of(kc), wl.k_cache) and np.array_equal(bits_of(vc), wl.v_cache)
