@@ -36,7 +36,9 @@
 // A buffer descriptor ends at the split's last key, so keys past it (another
 // split, the poisoned tail of a page, the end of a dense tensor) read as zero
 // without a fault.  The physical page of each tile comes from the block
-// table, 64 tiles' worth per vector load, broadcast with readlane.
+// table, 64 tiles' worth per vector load, broadcast with readlane.  A launch
+// that also appends keys to the cache (APP) ends the descriptors at the
+// cached keys and puts the new rows into the slots from k_new / v_new.
 //
 // Packed query rows beyond the unit's real rows are zero; their lanes do the
 // same (SIMD) work and are never written.  A workgroup carries one, two or
