@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--no-length-sum", action="store_true",
                     help="paged: do not give the planner the sum of the lengths")
     ap.add_argument("--pools", type=int, default=4, help="KV pool copies rotated over")
+    ap.add_argument("--new-keys", type=int, default=0,
+                    help="paged: each step appends this many keys a sequence in the same call "
+                         "(attn_decode_kvcache_fwd; the last N keys of every sequence come "
+                         "from k_new / v_new, holding the same values, so every step writes "
+                         "the same bytes and attends the same keys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
@@ -105,15 +110,36 @@ def main():
         # a serving loop knows its lengths on the host; their sum lets the
         # planner split the longest sequences of a ragged batch
         hint = None if args.no_length_sum else int(wl.cache_seqlens.sum())
-        first = api.PreparedDecode(q, pools[0][0], pools[0][1], bt, sl,
+        kn = vn = None
+        sl_call = sl
+        if args.new_keys > 0:
+            # the cache holds L_b - N keys before the call; the last N rows
+            # of each sequence come in as k_new / v_new (the same values)
+            N = args.new_keys
+            if int(wl.cache_seqlens.min()) < N:
+                print("--new-keys %d: a sequence of this workload has fewer keys" % N,
+                      file=sys.stderr)
+                sys.exit(2)
+            old = (wl.cache_seqlens - N).astype(np.int32)
+            shape = (wl.batch, N) + wl.k_cache.shape[2:]
+            kb, vb = np.zeros(shape, np.uint16), np.zeros(shape, np.uint16)
+            for b in range(wl.batch):
+                for t in range(N):
+                    pos = int(old[b]) + t
+                    pg, slot = wl.block_table[b, pos // wl.page_size], pos % wl.page_size
+                    kb[b, t], vb[b, t] = wl.k_cache[pg, slot], wl.v_cache[pg, slot]
+            kn, vn = dev16(kb), dev16(vb)
+            sl_call = torch.from_numpy(old).to(dev)
+        first = api.PreparedDecode(q, pools[0][0], pools[0][1], bt, sl_call,
                                    num_splits=args.num_splits, softmax_scale=wl.scale,
                                    max_seqlen_k=wl.max_seqlen_k, out=out, lse=lse, stream=stream,
-                                   sum_seqlen_k=hint)
-        calls = [first] + [api.PreparedDecode(q, kc, vc, bt, sl, num_splits=args.num_splits,
+                                   sum_seqlen_k=hint, k_new=kn, v_new=vn)
+        calls = [first] + [api.PreparedDecode(q, kc, vc, bt, sl_call,
+                                              num_splits=args.num_splits,
                                               softmax_scale=wl.scale,
                                               max_seqlen_k=wl.max_seqlen_k, out=out, lse=lse,
                                               workspace=first.workspace, stream=stream,
-                                              sum_seqlen_k=hint)
+                                              sum_seqlen_k=hint, k_new=kn, v_new=vn)
                            for kc, vc in pools[1:]]
 
     def step(i):
@@ -182,11 +208,15 @@ def main():
                   wl.num_heads_q, "num_heads_kv": wl.num_heads_kv, "q_len": wl.q_len,
                   "kv_len": wl.kv_len, "head_dim": wl.head_dim}
     else:
-        config = {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len,
+        name = wl.name + ("_append%d" % args.new_keys if args.new_keys > 0 else "")
+        config = {"workload": name, "batch": wl.batch, "q_len": wl.q_len,
                   "num_heads_q": wl.num_heads_q, "num_heads_kv": wl.num_heads_kv,
                   "head_dim": wl.head_dim, "page_size": wl.page_size,
                   "kv_tokens": int(wl.cache_seqlens.sum()),
                   "length_sum_given": not args.no_length_sum}
+        if args.new_keys > 0:
+            config.update({"new_keys": args.new_keys,
+                           "appended_in_kernel": last.kernel >= 100000})
     config.update({"kv_bytes": kv_bytes, "num_splits": last.num_splits,
                    "pack_gqa": last.pack_gqa, "heads_per_row": last.heads_per_row,
                    "extra_blocks": last.extra_blocks, "grid": last.grid,
@@ -219,9 +249,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(wl.name, last.num_splits),
+            "traffic": measured_traffic(config["workload"], last.num_splits),
             "kernel_avg_us": round(kern_s * 1e6, 3),
-            "kernels_per_launch": 1,
+            "kernels_per_launch": 2 if args.new_keys > 0 and last.kernel < 100000 else 1,
         },
         "single_launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "n": n_one,
                              "method": "event pair around each launch, host-paced"},

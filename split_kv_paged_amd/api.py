@@ -295,16 +295,28 @@ class PreparedDecode:
 
     Holds the shape struct and pointers of one set of tensors; each call
     re-enters attn_decode_fwd (which plans and validates again on the host)
-    with only the KV pointers optionally swapped.  The tensors must stay
-    alive and keep their shapes for the object's lifetime.
+    with only the KV pointers optionally swapped; with causal or k_new /
+    v_new (keys appended at cache_seqlens[b].., as in decode_fwd) it is
+    attn_decode_kvcache_fwd.  The tensors must stay alive and keep their
+    shapes for the object's lifetime.
     """
 
     def __init__(self, q, k_cache, v_cache, block_table, cache_seqlens, num_splits=0,
                  pack_gqa=-1, softmax_scale=None, max_seqlen_k=None, out=None, lse=None,
-                 workspace=None, stream=None, causal=False, sum_seqlen_k=None):
+                 workspace=None, stream=None, causal=False, sum_seqlen_k=None, k_new=None,
+                 v_new=None):
         _need(q.dtype in _DT and k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
               "q, k_cache, v_cache must share fp16 or bf16")
         dev = _check_dev(q, k_cache, v_cache, block_table, cache_seqlens, out, lse, workspace)
+        new_len = 0
+        if k_new is not None:
+            _need(v_new is not None and k_new.shape == v_new.shape and k_new.dim() == 4
+                  and k_new.shape[0] == q.shape[0] and k_new.shape[2:] == k_cache.shape[2:]
+                  and k_new.dtype == q.dtype and v_new.dtype == q.dtype
+                  and k_new.is_contiguous() and v_new.is_contiguous()
+                  and k_new.device == dev and v_new.device == dev,
+                  "k_new / v_new must be contiguous [B, new_len, Hkv, d] of q's dtype")
+            new_len = int(k_new.shape[1])
         self.shape = decode_shape(q, k_cache, block_table, max_seqlen_k, sum_seqlen_k)
         self.lib = _L.load()
         plan = _L.Plan()
@@ -319,14 +331,14 @@ class PreparedDecode:
             if workspace is None and plan.workspace_bytes > 0:
                 workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
         self.workspace = workspace
-        self._keep = (q, k_cache, v_cache, block_table, cache_seqlens)
+        self._keep = (q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new)
         tail = [int(num_splits), int(pack_gqa), float(softmax_scale) if softmax_scale else 0.0,
                 _ptr(self.out), _ptr(self.lse), _ptr(workspace),
                 workspace.numel() if workspace is not None else 0, _stream(dev, stream)]
         head = [ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                 _ptr(block_table), _ptr(cache_seqlens)]
-        if causal:  # attn_decode_kvcache_fwd with no appended keys
-            self.args = head + [None, None, 0, 1] + tail
+        if causal or new_len:  # attn_decode_kvcache_fwd
+            self.args = head + [_ptr(k_new), _ptr(v_new), new_len, int(bool(causal))] + tail
             self.fn = self.lib.attn_decode_kvcache_fwd
         else:
             self.args = head + tail
