@@ -6,7 +6,7 @@
 // sequence, in the pages the block table maps there (PA_BBND layout of the
 // MixedQuantSparseFlashMla article, section 参数说明), before attention
 // reads the cache.  One workgroup per (sequence, new key) copies the Hkv
-// rows of K and V; the data is small, so 16-bit element copies are enough.
+// rows of K and V, in 16-byte chunks where the row length allows.
 // The split kernel writes up to kMaxFusedNew keys a sequence itself where it
 // can (split_mfma.hip); this kernel covers the other calls.
 #include "internal.h"
@@ -28,9 +28,25 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + src;
   uint16_t* kc = static_cast<uint16_t*>(p.k_cache) + dst;
   uint16_t* vc = static_cast<uint16_t*>(p.v_cache) + dst;
+  if (n % 8 == 0) {
+    // 16-byte chunks: the rows start 16-byte aligned (aligned bases, rows of
+    // a multiple of 8 elements); each thread loads before it stores, so its
+    // loads are in flight together
+    const uint4* __restrict__ kn4 = reinterpret_cast<const uint4*>(kn);
+    const uint4* __restrict__ vn4 = reinterpret_cast<const uint4*>(vn);
+    uint4* __restrict__ kc4 = reinterpret_cast<uint4*>(kc);
+    uint4* __restrict__ vc4 = reinterpret_cast<uint4*>(vc);
+    for (int e = threadIdx.x; e < n / 8; e += blockDim.x) {
+      const uint4 kv = kn4[e], vv = vn4[e];
+      kc4[e] = kv;
+      vc4[e] = vv;
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    kc[e] = kn[e];
-    vc[e] = vn[e];
+    const uint16_t kv = kn[e], vv = vn[e];
+    kc[e] = kv;
+    vc[e] = vv;
   }
 }
 
