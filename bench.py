@@ -81,6 +81,10 @@ def main():
 
     wl = make_workload(args.workload, args.kv_len)
     dense = args.workload in ("c1", "c2")
+    if dense and args.new_keys > 0:
+        print("--new-keys appends to a paged cache: use a paged workload (c3, c4, c5)",
+              file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
