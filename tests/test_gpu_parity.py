@@ -1005,6 +1005,55 @@ def test_hip_graph_replays_match_eager(length_sum, d):
         assert np.array_equal(call.lse.cpu().numpy(), ref_l), "replay %d" % rep
 
 
+@pytest.mark.parametrize("new_len", [1, 5])
+def test_hip_graph_replays_with_appended_keys(new_len):
+    """A 4-split kvcache call (new keys written by the attention launch
+    itself with 1 key a sequence, by the append kernel first with 5)
+    captured in a HIP graph: before each replay the new rows are poisoned
+    again in the cache; every replay writes them back and equals the eager
+    result."""
+    dt = "bf16"
+    wl, k_new, v_new, kc_h, vc_h = _append_case(1850 + new_len, dt, 4, 1, 32, 8, 128,
+                                                [700, 33, 1500, 1], new_len)
+    q = to_dev(wl.q, dt)
+    kc, vc = to_dev(kc_h, dt), to_dev(vc_h, dt)
+    kc0, vc0 = kc.clone(), vc.clone()
+    bt, old = i32_dev(wl.block_table), i32_dev(np.array([700, 33, 1500, 1], dtype=np.int32))
+    kn, vn = to_dev(k_new, dt), to_dev(v_new, dt)
+    case("HIP graph capture of a 4-split kvcache call, %d new keys, 5 replays" % new_len)
+    mk = lambda **kw: api.PreparedDecode(q, kc, vc, bt, old, num_splits=4,
+                                         softmax_scale=wl.scale, max_seqlen_k=1500 + new_len,
+                                         k_new=kn, v_new=vn, **kw)
+    call = mk()
+    call()
+    torch.cuda.synchronize()
+    assert (api.last_plan().kernel >= 100000) == (new_len == 1)
+    ref_o, ref_l = bits_of(call.out).copy(), call.lse.cpu().numpy().copy()
+    assert np.array_equal(bits_of(kc), wl.k_cache) and np.array_equal(bits_of(vc), wl.v_cache)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the side stream, as graph capture wants
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    graph_call = mk(out=call.out, lse=call.lse, workspace=call.workspace)
+    with torch.cuda.graph(g):
+        graph_call.args[-1] = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        graph_call()
+    for rep in range(5):
+        call.out.zero_()
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(call.out), ref_o), "replay %d" % rep
+        assert np.array_equal(call.lse.cpu().numpy(), ref_l), "replay %d" % rep
+        assert np.array_equal(bits_of(kc), wl.k_cache), "replay %d" % rep
+        assert np.array_equal(bits_of(vc), wl.v_cache), "replay %d" % rep
+
+
 def test_side_stream_split_call():
     """A split call on a stream other than torch's current one: the binding
     allocates the outputs and zero-fills the workspace (the fused combine's
