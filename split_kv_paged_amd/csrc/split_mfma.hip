@@ -1083,11 +1083,13 @@ hipError_t launch_mfma_k(const SplitParams& prm, int grid, hipStream_t s,
   if (append && append->new_len > 0) {
     if constexpr (kDirect && PAGED) {
       if (append->new_len <= kMaxFusedNew && !prm.cu_q) {
-        const bool ex = prm.extra_blocks > 0;
-        const int plain = ex ? resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, false>>(NW)
-                             : resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, false>>(NW);
-        const int fused = ex ? resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, true>>(NW)
-                             : resident<mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, true>>(NW);
+        const bool ex = prm.extra_blocks > 0;  // the compact list's kernels
+        constexpr auto kPlain = mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, false>;
+        constexpr auto kPlainEx = mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, false>;
+        constexpr auto kApp = mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, false, true>;
+        constexpr auto kAppEx = mfma_split_kernel<DT, D, NW, NBUF, PAGED, GEN, NRB, true, true>;
+        const int plain = ex ? resident<kPlainEx>(NW) : resident<kPlain>(NW);
+        const int fused = ex ? resident<kAppEx>(NW) : resident<kApp>(NW);
         if (fused > 0 && (fused >= plain || grid <= (long)fused * append->num_cus)) {
           SplitParams p = prm;
           p.k_new = append->k_new;
