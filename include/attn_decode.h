@@ -193,7 +193,11 @@ typedef struct {
 /* Plan a paged decode call without touching any device.
  *   num_splits: 0 = choose by rule, >= 1 = use this value (<= 1024).
  *   pack_gqa:  -1 = choose by rule, 0 = off, 1 = on (forced on when S > 1).
- *   num_cus:    compute units to plan for; 0 = 256 (one MI355X).
+ *   num_cus:    compute units to plan for; 0 = 256 (one MI355X).  A caller
+ *               that counts workgroup slots instead passes compute units x
+ *               resident workgroups here and the plan's num_splits to the
+ *               forward call (the forward calls plan with the device's
+ *               compute units).
  * The rules are the lpnh.cn article's (section "pack_gqa 怎么选": row
  * efficiency with a 0.9 margin; section "num_splits 怎么选": one split when
  * the units reach 80% of the compute units or the KV spans at most 4 tiles
