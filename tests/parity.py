@@ -13,6 +13,8 @@ strict=True drops that allowance everywhere (plain max-abs), for workloads
 whose outputs stay below those magnitudes.
 Rows with no keys must be exactly O = 0, LSE = -inf.
 """
+import os
+
 import numpy as np
 import torch
 
@@ -22,6 +24,15 @@ ATOL = {"fp16": 2e-3, "bf16": 1e-2}
 LSE_ATOL = 1e-3
 PART_ATOL = 1e-3
 TORCH_DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+# (test id, what, max abs error, bar) of every passing check, for the raw
+# error table that tests/conftest.py prints after a run
+RECORDS = []
+
+
+def _record(what, err, bar):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    RECORDS.append((test, what, err, bar))
 
 
 def to_dev(bits, dtype, device="cuda"):
@@ -70,7 +81,9 @@ def check_out(got_bits, ref, dtype, what="out", strict=False):
         raise AssertionError("%s: %d/%d elements out of tolerance; worst at %s: gpu %r oracle %r "
                              "(max abs err %.3g)" % (what, bad.sum(), err.size, idx, got[idx],
                                                      ref[idx], err.max()))
-    return float(err.max()) if err.size else 0.0
+    worst = float(err.max()) if err.size else 0.0
+    _record(what, worst, ATOL[dtype] if strict else "%g+spacing" % ATOL[dtype])
+    return worst
 
 
 def check_lse(got, ref, what="lse", atol=LSE_ATOL):
@@ -82,6 +95,7 @@ def check_lse(got, ref, what="lse", atol=LSE_ATOL):
     if (~empty).any():
         err = np.abs(got[~empty] - ref[~empty])
         assert err.max() <= atol, "%s: max err %.3g" % (what, err.max())
+        _record(what, float(err.max()), atol)
         return float(err.max())
     return 0.0
 
