@@ -158,6 +158,36 @@ def test_paged_outliers_full_size(dt, S):
     assert_paged(wl, num_splits=S)
 
 
+# One batch holding sequence lengths from 1 to 8192 (tile edges and their
+# neighbours), over the pages' supported grid (fp16 and bf16, head dim 64 and
+# 128, GQA 2/4/8).  "ovf" widens the logits 30-fold through the softmax
+# scale: scores then reach about +-120, whose exponentials overflow float32
+# unless the running maximum is taken off first.
+MATRIX_LENS = [1, 2, 15, 16, 17, 255, 1023, 1025, 4096, 8191, 8192]
+
+
+@pytest.mark.parametrize("ovf", [False, True], ids=["n01", "ovf"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [2, 4, 8])
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_robustness_matrix(dt, G, d, ovf):
+    """The MXFlashAttn page's robustness matrix (section 快速复现: lengths 1
+    to 8192, GQA 2/4/8, bf16, overflow) over the shapes of its 能力矩阵
+    table, each case called three ways: the pages' split rule, the rule with
+    the length sum (ragged splits; head pairs at d 64) and four splits."""
+    scale = (30.0 if ovf else 1.0) / np.sqrt(d)
+    seed = 7100 + 8 * d + G + (1000 if ovf else 0) + (500 if dt == "fp16" else 0)
+    wl = W.make_paged(seed, dt, len(MATRIX_LENS), 1, 2 * G, 2, d, 16, MATRIX_LENS,
+                      spare_pages=2, scale=scale,
+                      name="matrix-%s-G%d-d%d-%s" % (dt, G, d, "ovf" if ovf else "n01"))
+    case("%s: lengths %s, softmax scale %.4g" % (wl.name, MATRIX_LENS, scale))
+    ref = oracle_paged(wl)
+    if ovf:  # the premise: some row's log-sum-exp lies beyond float32's exp range
+        assert ref[1].max() > 89.0, ref[1].max()
+    for S, hint in ((0, False), (0, True), (4, False)):
+        assert_paged(wl, num_splits=S, ref=ref, sum_hint=hint)
+
+
 def test_dense_decode_fp16():
     wl = W.c1_dense_decode()
     case("dense fp16 Hq8/Hkv2 d64 kvLen512 scale 1/8, num_splits=1")
