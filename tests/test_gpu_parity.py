@@ -223,6 +223,32 @@ def test_smallq_mha_fp16(kv_len):
         check_lse(lse.cpu().numpy(), ref_l)
 
 
+@pytest.mark.parametrize("ovf", [False, True], ids=["n01", "ovf"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_dense_robustness_matrix(dt, d, G, ovf):
+    """The robustness matrix on the dense small-query path (q_len 4): kvLen
+    1, 17, 1025 and 8192, MHA and GQA 2/4/8, both types, with N(0,1) logits
+    and with logits widened 30-fold ("ovf", as for the paged matrix); the
+    planner's split count and three splits."""
+    scale = (30.0 if ovf else 1.0) / np.sqrt(d)
+    for kv_len in (1, 17, 1025, 8192):
+        seed = 7300 + kv_len + 4 * d + G + (100 if ovf else 0) + (50 if dt == "fp16" else 0)
+        wl = W.make_dense(seed, dt, 2 * G, 2, 4, kv_len, d, scale=scale)
+        ref_o, ref_l = oracle.dense_attention(wl.q, wl.k, wl.v, dt, scale=scale)
+        if ovf and kv_len >= 1025:  # the premise, as for the paged matrix
+            assert ref_l.max() > 89.0, ref_l.max()
+        q, k, v = to_dev(wl.q, dt), to_dev(wl.k, dt), to_dev(wl.v, dt)
+        for S in (0, 3):
+            case("dense %s Hq%d/Hkv2 q4 kvLen %d d%d scale %.4g S=%d" % (dt, 2 * G, kv_len, d,
+                                                                         scale, S))
+            out, lse = api.dense_fwd(q, k, v, num_splits=S, softmax_scale=scale)
+            torch.cuda.synchronize()
+            check_out(bits_of(out), ref_o, dt)
+            check_lse(lse.cpu().numpy(), ref_l)
+
+
 DENSE_ROWS = [
     # dtype, Hq, Hkv, q_len, kv_len, d: packed rows G * q_len per unit
     ("bf16", 8, 8, 40, 700, 128),    # MHA, 40 rows: a 64-row block (Q staged in LDS)
