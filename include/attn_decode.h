@@ -358,6 +358,18 @@ attn_status attn_check_paged_inputs(const attn_decode_shape* shape,
                                     const int32_t* cache_seqlens_host, int64_t num_pages,
                                     int32_t* bad_batch);
 
+/* The same host check for an attn_decode_kvcache_fwd call that appends
+ * new_len keys per sequence (the paged KV append of the MXFlashAttn page,
+ * section 能力矩阵): every sequence's cache_seqlens[b] + new_len keys must
+ * be <= max_seqlen_k and mapped by block-table entries in [0, num_pages).
+ * A call that breaks this bound loses the keys past its last split.
+ * new_len < 0 -> ATTN_ERR_ARG; otherwise as attn_check_paged_inputs, which
+ * is this check with new_len = 0. */
+attn_status attn_check_kvcache_inputs(const attn_decode_shape* shape,
+                                      const int32_t* block_table_host,
+                                      const int32_t* cache_seqlens_host, int64_t num_pages,
+                                      int new_len, int32_t* bad_batch);
+
 /* Plan recorded by the last successful forward call on this thread
  * (ATTN_ERR_ARG if none yet): which kernel ran, with what split count,
  * packing and grid.  This is the dispatch record the MXFlashAttn page asks

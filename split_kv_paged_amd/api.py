@@ -275,18 +275,19 @@ def workspace_partials(workspace, plan, nrows, head_dim):
     return o, l
 
 
-def check_paged_inputs(shape_args, block_table_host, cache_seqlens_host, num_pages):
-    """Host check of block_table / cache_seqlens ranges (numpy int32 arrays).
-    Returns (status_name, bad_batch)."""
+def check_paged_inputs(shape_args, block_table_host, cache_seqlens_host, num_pages, new_len=0):
+    """Host check of block_table / cache_seqlens ranges (numpy int32 arrays),
+    for a call that appends new_len keys per sequence (0: a plain decode
+    call).  Returns (status_name, bad_batch)."""
     import numpy as np
     shape = _L.DecodeShape(*shape_args)
     bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
     sl = np.ascontiguousarray(cache_seqlens_host, dtype=np.int32)
     bad = ctypes.c_int32(-1)
-    code = _L.load().attn_check_paged_inputs(ctypes.byref(shape),
-                                             bt.ctypes.data_as(ctypes.c_void_p),
-                                             sl.ctypes.data_as(ctypes.c_void_p),
-                                             int(num_pages), ctypes.byref(bad))
+    code = _L.load().attn_check_kvcache_inputs(ctypes.byref(shape),
+                                               bt.ctypes.data_as(ctypes.c_void_p),
+                                               sl.ctypes.data_as(ctypes.c_void_p),
+                                               int(num_pages), int(new_len), ctypes.byref(bad))
     return _L.STATUS[code], bad.value
 
 

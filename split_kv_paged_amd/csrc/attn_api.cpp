@@ -617,16 +617,18 @@ attn_status attn_combine_fwd(int num_splits, int batch, int q_len, int num_heads
   return ATTN_OK;
 }
 
-attn_status attn_check_paged_inputs(const attn_decode_shape* shape,
-                                    const int32_t* block_table_host,
-                                    const int32_t* cache_seqlens_host, int64_t num_pages,
-                                    int32_t* bad_batch) {
+attn_status attn_check_kvcache_inputs(const attn_decode_shape* shape,
+                                      const int32_t* block_table_host,
+                                      const int32_t* cache_seqlens_host, int64_t num_pages,
+                                      int new_len, int32_t* bad_batch) {
   attn_status st = check_decode_shape(shape);
   if (st != ATTN_OK) return st;
+  if (new_len < 0) return ATTN_ERR_ARG;
   if (!block_table_host || !cache_seqlens_host) return ATTN_ERR_NULL;
   for (int b = 0; b < shape->batch; ++b) {
-    const int L = cache_seqlens_host[b];
-    bool bad = L < 0 || L > shape->max_seqlen_k;
+    // keys the call covers: the cached ones plus those it appends
+    const int64_t L = int64_t(cache_seqlens_host[b]) + new_len;
+    bool bad = cache_seqlens_host[b] < 0 || L > shape->max_seqlen_k;
     const int64_t used = bad ? 0 : ceil_div(L, shape->page_size);
     for (int64_t t = 0; t < used && !bad; ++t) {
       const int32_t pg = block_table_host[int64_t(b) * shape->max_pages_per_seq + t];
@@ -638,6 +640,14 @@ attn_status attn_check_paged_inputs(const attn_decode_shape* shape,
     }
   }
   return ATTN_OK;
+}
+
+attn_status attn_check_paged_inputs(const attn_decode_shape* shape,
+                                    const int32_t* block_table_host,
+                                    const int32_t* cache_seqlens_host, int64_t num_pages,
+                                    int32_t* bad_batch) {
+  return attn_check_kvcache_inputs(shape, block_table_host, cache_seqlens_host, num_pages, 0,
+                                   bad_batch);
 }
 
 attn_status attn_last_plan(attn_plan* plan) {

@@ -22,7 +22,8 @@ EXPORTS = (
     "attn_decode_plan", "attn_decode_fwd", "attn_decode_fwd_noalloc", "attn_decode_kvcache_fwd",
     "attn_decode_varlen_fwd",
     "attn_dense_plan", "attn_dense_fwd",
-    "attn_combine_fwd", "attn_check_paged_inputs", "attn_last_plan", "attn_status_str",
+    "attn_combine_fwd", "attn_check_paged_inputs", "attn_check_kvcache_inputs",
+    "attn_last_plan", "attn_status_str",
     "attn_abi_version",
 )
 
@@ -82,6 +83,7 @@ def load():
         "attn_dense_fwd": ([sn, P, P, P, I, F, P, P, P, Z, P], I),
         "attn_combine_fwd": ([I, I, I, I, I, I, P, P, P, P, P], I),
         "attn_check_paged_inputs": ([sd, P, P, I64, ctypes.POINTER(ctypes.c_int32)], I),
+        "attn_check_kvcache_inputs": ([sd, P, P, I64, I, ctypes.POINTER(ctypes.c_int32)], I),
         "attn_last_plan": ([pl], I),
         "attn_status_str": ([I], ctypes.c_char_p),
         "attn_abi_version": ([], I),

@@ -133,6 +133,19 @@ int main() {
     const attn_status st = attn_check_paged_inputs(&s, bt.data(), sl.data(), num_pages, &bad);
     CHECK(st == ATTN_OK || st == ATTN_ERR_DATA, "paged check status");
     CHECK(st == ATTN_OK ? bad == -1 : (bad >= 0 && bad < s.batch), "bad batch index reported");
+    // with appended keys (lengths near INT32_MAX too: the sum must not wrap)
+    const int new_len = int(next_u32() % 24) - 2;
+    if (trial % 10 == 0) sl[0] = 0x7FFFFFF0;
+    bad = -1;
+    const attn_status st2 =
+        attn_check_kvcache_inputs(&s, bt.data(), sl.data(), num_pages, new_len, &bad);
+    if (new_len < 0) {
+      CHECK(st2 == ATTN_ERR_ARG && bad == -1, "kvcache check rejects new_len < 0");
+    } else {
+      CHECK(st2 == ATTN_OK || st2 == ATTN_ERR_DATA, "kvcache check status");
+      CHECK(st2 == ATTN_OK ? bad == -1 : (bad >= 0 && bad < s.batch), "kvcache bad batch index");
+      if (trial % 10 == 0) CHECK(st2 == ATTN_ERR_DATA && bad == 0, "huge length rejected");
+    }
   }
 
   // forward entry points: rejected before any device work

@@ -315,6 +315,23 @@ def test_check_paged_inputs(lib):
     assert api.check_paged_inputs(args, bt, np.array([1, 0], np.int32), 7) == \
         ("ATTN_ERR_DATA", 0)
     assert api.check_paged_inputs(args, bt, np.array([0, 0], np.int32), 7) == ("ATTN_OK", -1)
+    # appended keys count against max_seqlen_k and need mapped pages
+    bt[0, 0] = 0
+    assert api.check_paged_inputs(args, bt, np.array([60, 40], np.int32), 7, new_len=4) == \
+        ("ATTN_OK", -1)
+    assert api.check_paged_inputs(args, bt, np.array([61, 40], np.int32), 7, new_len=4) == \
+        ("ATTN_ERR_DATA", 0)
+    assert api.check_paged_inputs(args, bt, np.array([60, 45], np.int32), 7, new_len=4) == \
+        ("ATTN_ERR_DATA", 1)
+    assert api.check_paged_inputs(args, bt, np.array([0, 0], np.int32), 7, new_len=-1) == \
+        ("ATTN_ERR_ARG", -1)
+    # the plain check is the same with new_len = 0, through its own symbol
+    shape = L.DecodeShape(*args)
+    sl = np.array([64, 48], np.int32)
+    bad = ctypes.c_int32(-1)
+    assert lib.attn_check_paged_inputs(ctypes.byref(shape), bt.ctypes.data_as(ctypes.c_void_p),
+                                       sl.ctypes.data_as(ctypes.c_void_p), 7,
+                                       ctypes.byref(bad)) == 0
 
 
 # The ragged-batch refinement (not from the pages): with the sum of the
